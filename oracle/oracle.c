@@ -1,0 +1,344 @@
+/*
+ * CPU oracle for the attention forward pass -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only tests, the smoke check and the benchmark's CPU-baseline leg may load this
+ * code.  It shares nothing with the GPU library: no headers, no helpers, no
+ * tables.  Everything is double precision, row by row, with no blocking beyond
+ * what each definition states.
+ *
+ * Tensor layouts (the pages' [batch, seqlen, heads, head_dim] convention, from
+ * "flash attention V2 code walk-through", tensor-shape table):
+ *   q [B, Sq, Hq, d]   k, v [B, Sk, Hkv, d]   o [B, Sq, Hq, d]   lse [B, Hq, Sq]
+ * Inputs are either double arrays (in_bf16 = 0) or bf16 bit patterns
+ * (in_bf16 = 1), which are widened exactly to double.
+ *
+ * Definitions followed:
+ *  - Scores s_j = scale * <q_i, k_j> and O = softmax(s) V, with the full score
+ *    row and probability row materialised: "FlashAttention 1, 2, 3" explainer,
+ *    shape section (S = QK^T/sqrt(d), P = softmax_rows(S + mask), O = PV) and
+ *    the naive three-step section.  `scale` replaces 1/sqrt(d) as given.
+ *  - GQA: query head h reads key/value head h / (Hq/Hkv) ("flash attention V2
+ *    code walk-through", parallelism section: the decode reshape groups
+ *    consecutive query heads per KV head).
+ *  - Causal mask aligned to the bottom-right: key j is visible to query i iff
+ *    j <= i + Sk - Sq ("03 forward CUDA kernel" section 8; walk-through
+ *    Is_causal mask pictures for Sq=2,Sk=5 and Sq=5,Sk=2).  Masked scores are
+ *    set to -inf after scaling and before the max (explainer, causal/tail
+ *    section).
+ *  - A row with no visible key returns O = 0 and LSE = -inf (explainer,
+ *    one-row runnable logic; forward-kernel page section 7.3).
+ *  - LSE = m + ln(l), natural log (explainer, one-row runnable logic and the
+ *    backward-recompute section).
+ *  - Online variant: the explainer's per-row loop over key tiles with state
+ *    (m, l, o), alpha = exp(m - m') applied to both l and o, fully masked tiles
+ *    skipped, alpha taken as 0 on the first tile with a valid key.
+ *  - Split variant: the key tiles are cut into num_splits contiguous ranges of
+ *    ceil(n_tiles / num_splits) tiles (walk-through, split-KV block range);
+ *    each range yields (O_s, LSE_s) or (0, -inf) when empty; the combine takes
+ *    LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s
+ *    (forward-kernel page section 7.3).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int in_bf16;
+  const void *q, *k, *v;
+  int B, Sq, Sk, Hq, Hkv, d, causal;
+  double scale;
+} problem;
+
+static double elem(const void *base, int in_bf16, int64_t idx) {
+  if (in_bf16) {
+    uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+  }
+  return ((const double *)base)[idx];
+}
+
+static int check(const problem *p) {
+  if (!p->q || !p->k || !p->v) return 1;
+  if (p->B < 0 || p->Sq < 0 || p->Sk < 0 || p->Hq < 1 || p->Hkv < 1 || p->d < 1) return 2;
+  if (p->Hq % p->Hkv != 0) return 3;
+  return 0;
+}
+
+static int64_t q_index(const problem *p, int b, int i, int h, int c) {
+  return (((int64_t)b * p->Sq + i) * p->Hq + h) * p->d + c;
+}
+
+static int64_t kv_index(const problem *p, int b, int j, int hk, int c) {
+  return (((int64_t)b * p->Sk + j) * p->Hkv + hk) * p->d + c;
+}
+
+static int kv_head(const problem *p, int h) { return h / (p->Hq / p->Hkv); }
+
+/* Visibility of key j to query i under the bottom-right causal convention. */
+static int visible(const problem *p, int i, int j) {
+  if (!p->causal) return 1;
+  return j <= i + p->Sk - p->Sq;
+}
+
+/* Scaled score of query (b,i,h) against key j. */
+static double score(const problem *p, int b, int h, int i, int j) {
+  int hk = kv_head(p, h);
+  double acc = 0.0;
+  for (int c = 0; c < p->d; ++c)
+    acc += elem(p->q, p->in_bf16, q_index(p, b, i, h, c)) *
+           elem(p->k, p->in_bf16, kv_index(p, b, j, hk, c));
+  return p->scale * acc;
+}
+
+/* Full score row S[0..Sk) with the mask applied, and its probability row P.
+ * Returns the number of visible keys; m and l receive max and sum of exp. */
+static int prob_row(const problem *p, int b, int h, int i, double *s, double *prob,
+                    double *m_out, double *l_out) {
+  int nvis = 0;
+  for (int j = 0; j < p->Sk; ++j) s[j] = score(p, b, h, i, j);
+  for (int j = 0; j < p->Sk; ++j) {
+    if (visible(p, i, j))
+      ++nvis;
+    else
+      s[j] = -INFINITY;
+  }
+  if (nvis == 0) {
+    for (int j = 0; j < p->Sk; ++j) prob[j] = 0.0;
+    *m_out = -INFINITY;
+    *l_out = 0.0;
+    return 0;
+  }
+  double m = -INFINITY;
+  for (int j = 0; j < p->Sk; ++j)
+    if (s[j] > m) m = s[j];
+  double l = 0.0;
+  for (int j = 0; j < p->Sk; ++j) {
+    prob[j] = exp(s[j] - m);
+    l += prob[j];
+  }
+  for (int j = 0; j < p->Sk; ++j) prob[j] /= l;
+  *m_out = m;
+  *l_out = l;
+  return nvis;
+}
+
+/* One row of the plain definition: O[i,:] = P V and LSE = m + ln l. */
+static void oneshot_row(const problem *p, int b, int h, int i, double *s, double *prob,
+                        double *o_row, double *lse) {
+  double m, l;
+  int nvis = prob_row(p, b, h, i, s, prob, &m, &l);
+  if (nvis == 0) {
+    for (int c = 0; c < p->d; ++c) o_row[c] = 0.0;
+    *lse = -INFINITY;
+    return;
+  }
+  int hk = kv_head(p, h);
+  for (int c = 0; c < p->d; ++c) {
+    double acc = 0.0;
+    for (int j = 0; j < p->Sk; ++j)
+      acc += prob[j] * elem(p->v, p->in_bf16, kv_index(p, b, j, hk, c));
+    o_row[c] = acc;
+  }
+  *lse = m + log(l);
+}
+
+/* The explainer's per-row online loop over key tiles [t_lo, t_hi) of size blk.
+ * Produces the normalised row output and its LSE, or (0, -inf). */
+static void online_row(const problem *p, int b, int h, int i, int blk, int t_lo, int t_hi,
+                       double *s, double *o_row, double *lse) {
+  int hk = kv_head(p, h);
+  double m = -INFINITY, l = 0.0;
+  for (int c = 0; c < p->d; ++c) o_row[c] = 0.0;
+  for (int t = t_lo; t < t_hi; ++t) {
+    int j0 = t * blk;
+    int j1 = j0 + blk < p->Sk ? j0 + blk : p->Sk;
+    int any = 0;
+    double tile_max = -INFINITY;
+    for (int j = j0; j < j1; ++j) {
+      double sj = score(p, b, h, i, j);
+      if (!visible(p, i, j)) sj = -INFINITY;
+      else any = 1;
+      s[j - j0] = sj;
+      if (sj > tile_max) tile_max = sj;
+    }
+    if (!any) continue; /* fully masked tile: skipped */
+    double m2 = m > tile_max ? m : tile_max;
+    double alpha = (l != 0.0) ? exp(m - m2) : 0.0;
+    double psum = 0.0;
+    for (int j = j0; j < j1; ++j) {
+      s[j - j0] = exp(s[j - j0] - m2);
+      psum += s[j - j0];
+    }
+    for (int c = 0; c < p->d; ++c) {
+      double pv = 0.0;
+      for (int j = j0; j < j1; ++j)
+        pv += s[j - j0] * elem(p->v, p->in_bf16, kv_index(p, b, j, hk, c));
+      o_row[c] = alpha * o_row[c] + pv;
+    }
+    l = alpha * l + psum;
+    m = m2;
+  }
+  if (l == 0.0) {
+    for (int c = 0; c < p->d; ++c) o_row[c] = 0.0;
+    *lse = -INFINITY;
+    return;
+  }
+  for (int c = 0; c < p->d; ++c) o_row[c] /= l;
+  *lse = m + log(l);
+}
+
+#define SETUP_PROBLEM                                                                    \
+  problem P = {in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale};                \
+  int err = check(&P);                                                                   \
+  if (err) return err;
+
+/* Plain definition over all rows. o [B,Sq,Hq,d], lse [B,Hq,Sq]. */
+int oracle_attn_fwd(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
+                    int Sk, int Hq, int Hkv, int d, int causal, double scale, double *o,
+                    double *lse) {
+  SETUP_PROBLEM
+  int64_t nrows = (int64_t)B * Hq * Sq;
+  #pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+    double *prob = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+    #pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+      int b = (int)(r / ((int64_t)Hq * Sq));
+      int h = (int)((r / Sq) % Hq);
+      int i = (int)(r % Sq);
+      oneshot_row(&P, b, h, i, s, prob, o + q_index(&P, b, i, h, 0),
+                  lse + ((int64_t)b * Hq + h) * Sq + i);
+    }
+    free(s);
+    free(prob);
+  }
+  return 0;
+}
+
+/* Plain definition on selected rows.  rows holds nrows triples (b, h, i);
+ * o_rows [nrows, d], lse_rows [nrows]. */
+int oracle_attn_rows(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
+                     int Sk, int Hq, int Hkv, int d, int causal, double scale, int nrows,
+                     const int *rows, double *o_rows, double *lse_rows) {
+  SETUP_PROBLEM
+  for (int r = 0; r < nrows; ++r) {
+    int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+    if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= Sq) return 4;
+  }
+  #pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+    double *prob = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+    #pragma omp for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r)
+      oneshot_row(&P, rows[3 * r], rows[3 * r + 1], rows[3 * r + 2], s, prob,
+                  o_rows + (int64_t)r * d, lse_rows + r);
+    free(s);
+    free(prob);
+  }
+  return 0;
+}
+
+/* The probability row P[b,h,i,:] of the plain definition (zeros if no key is visible). */
+int oracle_attn_probs(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
+                      int Sk, int Hq, int Hkv, int d, int causal, double scale, int b, int h,
+                      int i, double *prob) {
+  SETUP_PROBLEM
+  if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= Sq) return 4;
+  double *s = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+  double m, l;
+  prob_row(&P, b, h, i, s, prob, &m, &l);
+  free(s);
+  return 0;
+}
+
+/* Online (tiled) variant with key tile size blk. */
+int oracle_attn_online(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
+                       int Sk, int Hq, int Hkv, int d, int causal, double scale, int blk,
+                       double *o, double *lse) {
+  SETUP_PROBLEM
+  if (blk < 1) return 5;
+  int ntiles = (Sk + blk - 1) / blk;
+  int64_t nrows = (int64_t)B * Hq * Sq;
+  #pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * blk);
+    #pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+      int b = (int)(r / ((int64_t)Hq * Sq));
+      int h = (int)((r / Sq) % Hq);
+      int i = (int)(r % Sq);
+      online_row(&P, b, h, i, blk, 0, ntiles, s, o + q_index(&P, b, i, h, 0),
+                 lse + ((int64_t)b * Hq + h) * Sq + i);
+    }
+    free(s);
+  }
+  return 0;
+}
+
+/* Split-KV variant: num_splits contiguous tile ranges, each run with the online
+ * loop, then the LSE-weighted combine.  o_part [S,B,Hq,Sq,d] and lse_part
+ * [S,B,Hq,Sq] receive the per-split results (either may be NULL); o, lse the
+ * combined result. */
+int oracle_attn_split(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
+                      int Sk, int Hq, int Hkv, int d, int causal, double scale, int blk,
+                      int num_splits, double *o_part, double *lse_part, double *o,
+                      double *lse) {
+  SETUP_PROBLEM
+  if (blk < 1) return 5;
+  if (num_splits < 1) return 6;
+  int ntiles = (Sk + blk - 1) / blk;
+  int per_split = (ntiles + num_splits - 1) / num_splits;
+  int64_t nrows = (int64_t)B * Hq * Sq;
+  #pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * blk);
+    double *os = (double *)malloc(sizeof(double) * num_splits * d);
+    double *ls = (double *)malloc(sizeof(double) * num_splits);
+    #pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+      int b = (int)(r / ((int64_t)Hq * Sq));
+      int h = (int)((r / Sq) % Hq);
+      int i = (int)(r % Sq);
+      for (int sp = 0; sp < num_splits; ++sp) {
+        int t_lo = sp * per_split;
+        int t_hi = t_lo + per_split < ntiles ? t_lo + per_split : ntiles;
+        if (t_lo > t_hi) t_lo = t_hi;
+        online_row(&P, b, h, i, blk, t_lo, t_hi, s, os + (int64_t)sp * d, ls + sp);
+        int64_t prow = (((int64_t)sp * B + b) * Hq + h) * Sq + i;
+        if (o_part)
+          memcpy(o_part + prow * d, os + (int64_t)sp * d, sizeof(double) * d);
+        if (lse_part) lse_part[prow] = ls[sp];
+      }
+      /* combine */
+      double lmax = -INFINITY;
+      for (int sp = 0; sp < num_splits; ++sp)
+        if (ls[sp] > lmax) lmax = ls[sp];
+      double *orow = o + q_index(&P, b, i, h, 0);
+      double *lrow = lse + ((int64_t)b * Hq + h) * Sq + i;
+      if (lmax == -INFINITY) {
+        for (int c = 0; c < d; ++c) orow[c] = 0.0;
+        *lrow = -INFINITY;
+        continue;
+      }
+      double sum = 0.0;
+      for (int sp = 0; sp < num_splits; ++sp) sum += exp(ls[sp] - lmax);
+      double L = lmax + log(sum);
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int sp = 0; sp < num_splits; ++sp)
+          acc += exp(ls[sp] - L) * os[(int64_t)sp * d + c];
+        orow[c] = acc;
+      }
+      *lrow = L;
+    }
+    free(s);
+    free(os);
+    free(ls);
+  }
+  return 0;
+}

@@ -1,0 +1,341 @@
+"""Checks that pin the CPU oracle to what the pages and the mathematics fix.
+
+Each check takes an ``oracle.Oracle`` instance and raises AssertionError on failure.
+The same battery runs against the real oracle (every check must pass) and against
+mutated copies of it (each mutant must fail at least one check).
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+LN3 = math.log(3.0)
+TIGHT = 1e-12
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _num(x):
+    return {"0": 0.0, "ln3": LN3}[x] if isinstance(x, str) else float(x)
+
+
+def one_row(qv, ks, vs):
+    """A single query (d=1 per key score) as oracle inputs: q [1,1,1,1], k/v [1,n,1,1]."""
+    n = len(ks)
+    q = np.array(qv, dtype=np.float64).reshape(1, 1, 1, 1)
+    k = np.array(ks, dtype=np.float64).reshape(1, n, 1, 1)
+    v = np.array(vs, dtype=np.float64).reshape(1, n, 1, 1)
+    return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# Worked examples printed on the pages
+
+
+def check_online_softmax_example(orc):
+    g = golden("online_softmax_worked_example.json")
+    scores = sum(g["tile_scores"], [])
+    values = sum(g["tile_values"], [])
+    q, k, v = one_row([1.0], scores, values)
+    e = math.exp
+    exact = (2 * e(1) + 8 * e(2) + 4 * e(3) + 10 * e(0)) / (e(1) + e(2) + e(3) + e(0))
+    exact_lse = math.log(e(1) + e(2) + e(3) + 1.0)
+    tol_printed = 0.5 * 10 ** (-g["printed_digits"])
+    o, lse = orc.fwd(q, k, v, False, 1.0)
+    assert abs(o[0, 0, 0, 0] - g["printed_O"]) <= tol_printed, o
+    assert abs(o[0, 0, 0, 0] - exact) < TIGHT and abs(lse[0, 0, 0] - exact_lse) < TIGHT
+    o2, lse2 = orc.online(q, k, v, False, 1.0, 2)
+    assert abs(o2[0, 0, 0, 0] - exact) < TIGHT and abs(lse2[0, 0, 0] - exact_lse) < TIGHT
+    # Per-tile state: after tile 1, m = 2 with weights exp([-1, 0]).
+    op, lp, o3, l3 = orc.split(q, k, v, False, 1.0, 2, 2)
+    m1 = g["after_tile_1"]["m"]
+    w1 = [math.exp(x) for x in g["after_tile_1"]["weights_exponents"]]
+    l1 = sum(w1)
+    assert abs(lp[0, 0, 0, 0] - (m1 + math.log(l1))) < TIGHT
+    assert abs(op[0, 0, 0, 0, 0] - (w1[0] * 2 + w1[1] * 8) / l1) < TIGHT
+    assert abs(o3[0, 0, 0, 0] - exact) < TIGHT and abs(l3[0, 0, 0] - exact_lse) < TIGHT
+
+
+def check_one_query_two_keys(orc):
+    g = golden("one_query_two_keys.json")
+    ks = [_num(x) for x in g["k"]]
+    q, k, v = one_row(g["q"], ks, g["v"])
+    p = orc.probs(q, k, v, False, 1.0, 0, 0, 0)
+    assert np.allclose(p, g["printed_P"], rtol=0, atol=TIGHT), p
+    o, lse = orc.fwd(q, k, v, False, 1.0)
+    assert abs(o[0, 0, 0, 0] - g["printed_O"]) < TIGHT
+    assert abs(lse[0, 0, 0] - math.log(4.0)) < TIGHT
+    # The same scores through the scale argument: k = [0, 1], scale = ln 3.
+    q2, k2, v2 = one_row(g["q"], [0.0, 1.0], g["v"])
+    o2, lse2 = orc.fwd(q2, k2, v2, False, LN3)
+    assert abs(o2[0, 0, 0, 0] - g["printed_O"]) < TIGHT
+    assert abs(lse2[0, 0, 0] - math.log(4.0)) < TIGHT
+    o3, _ = orc.online(q2, k2, v2, False, LN3, 1)
+    assert abs(o3[0, 0, 0, 0] - g["printed_O"]) < TIGHT
+
+
+def check_exercise_1(orc):
+    g = golden("exercises.json")["exercise_1"]
+    s = [_num(g["block_A"]["s"]), _num(g["block_B"]["s"])]
+    vv = [g["block_A"]["v"], g["block_B"]["v"]]
+    q, k, v = one_row([1.0], s, vv)
+    correct = (1.0 * vv[0] + 3.0 * vv[1]) / 4.0          # weights e^0 : e^ln3 = 1 : 3
+    wrong = 0.5 * (vv[0] + vv[1])                         # average of the local outputs
+    assert correct == 4.0 and wrong == 6.0
+    for o, lse in (orc.fwd(q, k, v, False, 1.0), orc.online(q, k, v, False, 1.0, 1)):
+        assert abs(o[0, 0, 0, 0] - correct) < TIGHT and abs(lse[0, 0, 0] - math.log(4)) < TIGHT
+    op, lp, o, lse = orc.split(q, k, v, False, 1.0, 1, 2)
+    assert abs(op[0, 0, 0, 0, 0] - vv[0]) < TIGHT and abs(op[1, 0, 0, 0, 0] - vv[1]) < TIGHT
+    assert abs(lp[0, 0, 0, 0]) < TIGHT and abs(lp[1, 0, 0, 0] - LN3) < TIGHT
+    assert abs(o[0, 0, 0, 0] - correct) < TIGHT and abs(o[0, 0, 0, 0] - wrong) > 1.0
+
+
+def check_exercise_2(orc):
+    g = golden("exercises.json")["exercise_2"]
+    P = g["P"]
+    q, k, v = one_row([1.0], [math.log(x) for x in P], g["V"])
+    expect = sum(a * b for a, b in zip(P, g["V"]))
+    assert abs(expect - 3.6) < 1e-15
+    o, lse = orc.fwd(q, k, v, False, 1.0)
+    assert abs(o[0, 0, 0, 0] - expect) < TIGHT and abs(lse[0, 0, 0]) < TIGHT
+    assert np.allclose(orc.probs(q, k, v, False, 1.0, 0, 0, 0), P, rtol=0, atol=TIGHT)
+
+
+def check_causal_mask_pictures(orc):
+    for case in golden("causal_mask_pictures.json")["cases"]:
+        Sq, Sk = case["Sq"], case["Sk"]
+        mask = np.array(case["mask"])
+        q = np.zeros((1, Sq, 1, 1))
+        k = np.zeros((1, Sk, 1, 1))
+        v = np.arange(1, Sk + 1, dtype=np.float64).reshape(1, Sk, 1, 1)
+        o, lse = orc.fwd(q, k, v, True, 1.0)
+        for i in range(Sq):
+            p = orc.probs(q, k, v, True, 1.0, 0, 0, i)
+            assert np.array_equal(p > 0, mask[i] == 1), (case, i, p)
+            nvis = int(mask[i].sum())
+            if nvis == 0:
+                assert o[0, i, 0, 0] == 0.0 and lse[0, 0, i] == -np.inf
+            else:
+                assert abs(lse[0, 0, i] - math.log(nvis)) < TIGHT
+                assert abs(o[0, i, 0, 0] - np.mean(np.arange(1, nvis + 1))) < TIGHT
+
+
+def check_tail_tile_case(orc):
+    g = golden("tail_tile_case.json")
+    N, T, row = g["N"], g["tile"], g["row"]
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, N, 1, 3))
+    k = rng.standard_normal((1, N, 1, 3))
+    v = rng.standard_normal((1, N, 1, 3))
+    p = orc.probs(q, k, v, True, 0.5, 0, 0, row)
+    second = [j for j in range(T, min(2 * T, N)) if p[j] > 0]
+    assert second == g["valid_keys_in_second_tile"]
+    o1, l1 = orc.fwd(q, k, v, True, 0.5)
+    o2, l2 = orc.online(q, k, v, True, 0.5, T)
+    assert np.allclose(o1, o2, rtol=0, atol=TIGHT) and np.allclose(l1, l2, rtol=0, atol=TIGHT)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants
+
+
+def _rand(seed, B, Sq, Sk, Hq, Hkv, d):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, Sq, Hq, d)), rng.standard_normal((B, Sk, Hkv, d)),
+            rng.standard_normal((B, Sk, Hkv, d)))
+
+
+def check_special_cases(orc):
+    # Sk = 1: O = v0, LSE = s0.
+    q, k, v = _rand(1, 2, 3, 1, 2, 2, 5)
+    o, lse = orc.fwd(q, k, v, False, 0.7)
+    for b in range(2):
+        for h in range(2):
+            for i in range(3):
+                assert np.allclose(o[b, i, h], v[b, 0, h], rtol=0, atol=TIGHT)
+                assert abs(lse[b, h, i] - 0.7 * np.dot(q[b, i, h], k[b, 0, h])) < TIGHT
+    # Q = 0: uniform weights over the visible keys (causal, Sq < Sk).
+    q, k, v = _rand(2, 1, 4, 7, 1, 1, 3)
+    q[:] = 0.0
+    o, lse = orc.fwd(q, k, v, True, 1.3)
+    for i in range(4):
+        nvis = i + 7 - 4 + 1
+        assert np.allclose(o[0, i, 0], v[0, :nvis, 0].mean(axis=0), rtol=0, atol=TIGHT)
+        assert abs(lse[0, 0, i] - math.log(nvis)) < TIGHT
+    # V constant: O = c.
+    q, k, v = _rand(3, 1, 5, 6, 2, 1, 4)
+    v[:] = -2.5
+    o, _ = orc.fwd(q, k, v, True, 0.9)
+    assert np.allclose(o, -2.5, rtol=0, atol=TIGHT)
+    # Causal row 0 with Sq == Sk: O = v0.
+    q, k, v = _rand(4, 1, 6, 6, 1, 1, 4)
+    o, lse = orc.fwd(q, k, v, True, 0.5)
+    assert np.allclose(o[0, 0, 0], v[0, 0, 0], rtol=0, atol=TIGHT)
+
+
+def check_probability_rows(orc):
+    q, k, v = _rand(5, 1, 6, 9, 2, 2, 4)
+    for causal in (False, True):
+        o, lse = orc.fwd(q, k, v, causal, 0.6)
+        for h in range(2):
+            for i in range(6):
+                p = orc.probs(q, k, v, causal, 0.6, 0, h, i)
+                assert abs(p.sum() - 1.0) < TIGHT
+                assert np.allclose(o[0, i, h], p @ v[0, :, h], rtol=0, atol=TIGHT)
+                s = 0.6 * (k[0, :, h] @ q[0, i, h])
+                vis = np.arange(9) <= (i + 9 - 6) if causal else np.ones(9, bool)
+                smax = s[vis].max()
+                assert smax - TIGHT <= lse[0, h, i] <= smax + math.log(vis.sum()) + TIGHT
+                lo, hi = v[0, vis, h].min(axis=0), v[0, vis, h].max(axis=0)
+                assert np.all(o[0, i, h] >= lo - TIGHT) and np.all(o[0, i, h] <= hi + TIGHT)
+
+
+def check_shift_invariance(orc):
+    # Column d-1 of K is 1; adding c/scale to q[i, d-1] adds c to every score of row i.
+    q, k, v = _rand(6, 1, 4, 6, 1, 1, 5)
+    k[..., -1] = 1.0
+    scale, c = 0.8, 1.7
+    o1, l1 = orc.fwd(q, k, v, False, scale)
+    q2 = q.copy()
+    q2[..., -1] += c / scale
+    o2, l2 = orc.fwd(q2, k, v, False, scale)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-11)
+    assert np.allclose(l2 - l1, c, rtol=0, atol=1e-11)
+
+
+def check_key_permutation(orc):
+    q, k, v = _rand(7, 2, 3, 8, 2, 2, 4)
+    perm = np.random.default_rng(1).permutation(8)
+    o1, l1 = orc.fwd(q, k, v, False, 0.4)
+    o2, l2 = orc.fwd(q, k[:, perm], v[:, perm], False, 0.4)
+    assert np.allclose(o1, o2, rtol=0, atol=TIGHT) and np.allclose(l1, l2, rtol=0, atol=TIGHT)
+
+
+def check_gqa_grouping(orc):
+    # Query head h reads KV head h // (Hq/Hkv): same as MHA with each KV head repeated g times.
+    q, k, v = _rand(8, 2, 5, 6, 6, 2, 3)
+    o1, l1 = orc.fwd(q, k, v, True, 0.7)
+    o2, l2 = orc.fwd(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2), True, 0.7)
+    assert np.allclose(o1, o2, rtol=0, atol=TIGHT) and np.allclose(l1, l2, rtol=0, atol=TIGHT)
+    # and not the interleaved reading h % Hkv
+    o3, _ = orc.fwd(q, np.tile(k, (1, 1, 3, 1)), np.tile(v, (1, 1, 3, 1)), True, 0.7)
+    assert not np.allclose(o1, o3, rtol=0, atol=1e-6)
+
+
+def check_online_and_split_agree(orc):
+    for (B, Sq, Sk, Hq, Hkv, d, causal) in ((1, 7, 7, 1, 1, 3, True), (2, 5, 9, 4, 2, 4, True),
+                                            (1, 9, 4, 2, 2, 3, True), (2, 6, 11, 2, 1, 5, False)):
+        q, k, v = _rand(B * 100 + Sk, B, Sq, Sk, Hq, Hkv, d)
+        o, lse = orc.fwd(q, k, v, causal, 0.45)
+        for blk in (1, 2, 3, 4, 8, 64):
+            o2, l2 = orc.online(q, k, v, causal, 0.45, blk)
+            assert np.allclose(o, o2, rtol=0, atol=TIGHT), (blk, np.abs(o - o2).max())
+            assert np.array_equal(np.isneginf(lse), np.isneginf(l2))
+            fin = np.isfinite(lse)
+            assert np.allclose(lse[fin], l2[fin], rtol=0, atol=TIGHT)
+        for blk, S in ((1, 1), (2, 3), (3, 2), (1, 7), (4, 5), (2, 7)):
+            op, lp, o3, l3 = orc.split(q, k, v, causal, 0.45, blk, S)
+            assert np.allclose(o, o3, rtol=0, atol=TIGHT), (blk, S)
+            assert np.array_equal(np.isneginf(lse), np.isneginf(l3))
+            assert np.allclose(lse[np.isfinite(lse)], l3[np.isfinite(lse)], rtol=0, atol=TIGHT)
+            ntiles = -(-Sk // blk)
+            per = -(-ntiles // S)
+            for s in range(S):
+                if s * per >= ntiles:  # empty split -> (0, -inf)
+                    assert np.all(op[s] == 0.0) and np.all(np.isneginf(lp[s]))
+
+
+def check_rows_match_full(orc):
+    q, k, v = _rand(9, 2, 6, 7, 4, 2, 3)
+    o, lse = orc.fwd(q, k, v, True, 0.3)
+    rows = [(1, 3, 5), (0, 0, 0), (1, 1, 2), (0, 2, 4)]
+    orow, lrow = orc.rows(q, k, v, True, 0.3, rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.array_equal(orow[n], o[b, i, h]) and lrow[n] == lse[b, h, i]
+
+
+def check_bf16_widening(orc):
+    # bf16 bit patterns are widened exactly: same result as passing the float64 values.
+    rng = np.random.default_rng(11)
+    shape_q, shape_kv = (1, 3, 2, 4), (1, 5, 1, 4)
+    bits = [rng.integers(0, 1 << 16, size=s, dtype=np.uint16) & np.uint16(0xBFFF)
+            for s in (shape_q, shape_kv, shape_kv)]
+    bits = [np.where((b & 0x7F80) == 0x7F80, b & 0x3FFF, b).astype(np.uint16) for b in bits]
+    f64 = [((b.astype(np.uint32) << 16).view(np.float32)).astype(np.float64) for b in bits]
+    o1, l1 = orc.fwd(*bits, False, 0.01)
+    o2, l2 = orc.fwd(*f64, False, 0.01)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------
+# Brute force in 50-digit decimal arithmetic
+
+
+def decimal_attention(q, k, v, causal, scale):
+    getcontext().prec = 50
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    g = Hq // Hkv
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.zeros((B, Hq, Sq))
+    D = Decimal
+    sc = D(float(scale))
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            for i in range(Sq):
+                s = []
+                for j in range(Sk):
+                    if causal and j > i + Sk - Sq:
+                        continue
+                    acc = sum(D(float(q[b, i, h, c])) * D(float(k[b, j, hk, c])) for c in range(d))
+                    s.append((j, sc * acc))
+                if not s:
+                    lse[b, h, i] = -np.inf
+                    continue
+                m = max(x for _, x in s)
+                w = [(j, (x - m).exp()) for j, x in s]
+                l = sum(x for _, x in w)
+                for c in range(d):
+                    o[b, i, h, c] = float(sum(x * D(float(v[b, j, hk, c])) for j, x in w) / l)
+                lse[b, h, i] = float(m + l.ln())
+    return o, lse
+
+
+def check_decimal_brute_force(orc):
+    for seed, (B, Sq, Sk, Hq, Hkv, d, causal, scale) in enumerate(
+            ((1, 4, 4, 1, 1, 3, False, 0.5), (1, 5, 8, 2, 1, 4, True, 0.35),
+             (2, 8, 3, 2, 2, 2, True, 1.1), (1, 6, 7, 4, 2, 3, True, 0.8))):
+        q, k, v = _rand(100 + seed, B, Sq, Sk, Hq, Hkv, d)
+        od, ld = decimal_attention(q, k, v, causal, scale)
+        fin = np.isfinite(ld)
+        for o, lse in (orc.fwd(q, k, v, causal, scale), orc.online(q, k, v, causal, scale, 3),
+                       orc.split(q, k, v, causal, scale, 2, 3)[2:]):
+            assert np.allclose(o, od, rtol=0, atol=TIGHT), np.abs(o - od).max()
+            assert np.array_equal(np.isneginf(lse), ~fin)
+            assert np.allclose(lse[fin], ld[fin], rtol=0, atol=TIGHT)
+
+
+ALL_CHECKS = [
+    check_online_softmax_example, check_one_query_two_keys, check_exercise_1, check_exercise_2,
+    check_causal_mask_pictures, check_tail_tile_case, check_special_cases,
+    check_probability_rows, check_shift_invariance, check_key_permutation, check_gqa_grouping,
+    check_online_and_split_agree, check_rows_match_full, check_bf16_widening,
+    check_decimal_brute_force,
+]
+
+
+def failing_checks(orc):
+    failed = []
+    for chk in ALL_CHECKS:
+        try:
+            chk(orc)
+        except AssertionError:
+            failed.append(chk.__name__)
+    return failed

@@ -1,0 +1,32 @@
+"""Mutation tests: plant each mistake the explainer's CPU-lab section asks about into a
+copy of the oracle (dropping alpha on the old numerator, dropping the scale, turning the
+causal <= into <), rebuild it, and require at least one pin to fail."""
+import os
+
+import pytest
+
+import oracle as oracle_pkg
+import oracle_checks as oc
+
+MUTANTS = {
+    "drop_alpha_on_numerator": ("o_row[c] = alpha * o_row[c] + pv;", "o_row[c] = o_row[c] + pv;"),
+    "drop_scale": ("return p->scale * acc;", "return acc;"),
+    "causal_strict": ("return j <= i + p->Sk - p->Sq;", "return j < i + p->Sk - p->Sq;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle_pkg.SOURCE).read()
+    assert src.count(old) == 1, f"anchor for {name} not found exactly once"
+    mut_src = tmp_path / f"oracle_{name}.c"
+    mut_src.write_text(src.replace(old, new))
+    lib = str(tmp_path / f"liboracle_{name}.so")
+    oracle_pkg.build(src=str(mut_src), out=lib)
+    failed = oc.failing_checks(oracle_pkg.Oracle(lib))
+    assert failed, f"mutant {name} passed every check"
+
+
+def test_unmutated_oracle_passes_all(oracle):
+    assert oc.failing_checks(oracle) == []
