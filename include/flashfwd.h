@@ -1,0 +1,120 @@
+/*
+ * libflashfwd -- fused, tiled attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every tensor argument is a device pointer owned by the caller; the
+ * library never allocates, frees or synchronises, and keeps no mutable global
+ * state apart from a per-device cache of the compute-unit count.  Each call
+ * checks all of its arguments before enqueueing anything: on a non-zero return
+ * nothing was enqueued and no output was touched.  On success the work is
+ * enqueued on `stream` (a hipStream_t; NULL means the null stream) and runs
+ * asynchronously; device faults surface at the caller's next synchronisation
+ * with that stream.  Calls are re-entrant.  There is no fallback path: an
+ * unsupported shape is an error, never a slower route.
+ *
+ * Layouts (the pages' [batch, seqlen, heads, head_dim] convention: "flash
+ * attention V2 code walk-through", tensor-shape table), all row-major and
+ * contiguous:
+ *   q        bf16 [B, Sq, Hq, d]
+ *   k, v     bf16 [B, Sk, Hkv, d]
+ *   o        fp32 [B, Sq, Hq, d]
+ *   lse      fp32 [B, Hq, Sq]           natural-log logsumexp of the scaled scores
+ *   o_accum  fp32 [S, B, Hq, Sq, d]     per-split normalised partial outputs
+ *   lse_accum fp32 [S, B, Hq, Sq]       per-split logsumexp
+ * Query head h attends with key/value head h / (Hq / Hkv) (grouped-query
+ * attention; Hq must be a multiple of Hkv).
+ *
+ * Semantics shared by all entry points.  For query row i of head h:
+ *   s_j = scale * <q_i, k_j>;  key j is visible iff !causal or j <= i + Sk - Sq
+ *   (causal mask aligned to the bottom-right corner: "03 forward CUDA kernel",
+ *   section 8, and the walk-through's Is_causal pictures);
+ *   O_i = sum_j softmax(s)_j v_j over visible keys, LSE_i = log sum_j exp(s_j);
+ *   a row with no visible key gets O_i = 0 and LSE_i = -inf (explainer's
+ *   one-row loop; forward-kernel page section 7.3).
+ * S and P are never written to memory ("FlashAttention 1, 2, 3" explainer,
+ * tiling section; forward-kernel page sections 3-6).  Arithmetic: bf16 inputs,
+ * bf16 matrix-core products with fp32 accumulation, fp32 softmax state.
+ *
+ * Limits checked on every call: B, Sq, Sk >= 1; d in {64, 128}; Hq, Hkv >= 1;
+ * every pointer 16-byte aligned; scale finite and > 0; each tensor below 2^31
+ * elements.
+ */
+#ifndef FLASHFWD_H
+#define FLASHFWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FF_OK = 0,
+  FF_ERR_NULL = 1,     /* a required pointer is NULL */
+  FF_ERR_SHAPE = 2,    /* B, Sq, Sk, Hq or Hkv < 1, or a size over the limits */
+  FF_ERR_HEADDIM = 3,  /* d not in {64, 128} */
+  FF_ERR_GQA = 4,      /* Hq not a multiple of Hkv */
+  FF_ERR_ALIGN = 5,    /* a pointer not 16-byte aligned */
+  FF_ERR_SPLITS = 6,   /* num_splits outside [1, FF_MAX_SPLITS] */
+  FF_ERR_SCALE = 7,    /* scale not finite or not > 0 */
+  FF_ERR_HIP = 8,      /* the HIP runtime reported an error (device query or launch) */
+  FF_ERR_ALIAS = 9     /* an output overlaps an input */
+} ff_status;
+
+#define FF_MAX_SPLITS 128
+/* Key granularity of the split-KV partition: split s of S covers key blocks
+ * [s*ceil(nb/S), min((s+1)*ceil(nb/S), nb)) with nb = ceil(Sk / FF_SPLIT_BLOCK_N). */
+#define FF_SPLIT_BLOCK_N 128
+
+/* Fused forward pass (the prefill kernel): one workgroup per (query tile,
+ * batch, head) streams key/value tiles through LDS, updates the online-softmax
+ * state and accumulates O, then writes O = o / l and LSE = m + log l
+ * (forward-kernel page sections 2-6; explainer, online-softmax and one-row
+ * loop sections).  Writes o and lse in full. */
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
+             int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal, float scale,
+             void* stream);
+
+/* Split count for attn_fwd_splitkv.  The rule is the forward-kernel page's
+ * (section 7.2): the smallest split count whose wave efficiency is at least 85%
+ * of the best, where efficiency(S) = w / ceil(w) and w = units * S / slots.
+ * Here units = B * Hkv * ceil(Sq * (Hq/Hkv) / 16) workgroups per split and
+ * slots = num_cus * 2 workgroups resident at once, and S is capped so every
+ * split keeps at least 4 key blocks of FF_SPLIT_BLOCK_N.  num_cus <= 0 queries
+ * the current device.  Pure host arithmetic apart from that query.
+ * Returns S >= 1, or the negated ff_status on invalid arguments. */
+int attn_splitkv_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int d, int num_cus);
+
+/* The efficiency rule alone, for `units` workgroups per split on `slots`
+ * concurrent workgroup slots, searching S in [1, max_splits].  With units = 48,
+ * slots = 108 it returns 2 (efficiencies 0.89 at S = 2 and 0.67 at S = 3, the
+ * page's worked example).  Returns the negated FF_ERR_SHAPE if an argument < 1. */
+int attn_splits_efficiency_rule(int units, int slots, int max_splits);
+
+/* Split-KV forward (the decode kernel).  The key range is cut into num_splits
+ * contiguous ranges of FF_SPLIT_BLOCK_N-key blocks (walk-through, split-KV
+ * block range); each workgroup computes one range for up to 16 query rows of
+ * one key/value head, the Hq/Hkv query heads sharing that head folded into the
+ * row dimension (forward-kernel page section 7.4; the fold is a stride view, no
+ * copy).  num_splits == 1: writes o and lse directly (o_accum, lse_accum may be
+ * NULL).  num_splits > 1: writes o_accum and lse_accum only (o, lse may be
+ * NULL); a split with no visible key writes O_s = 0 and LSE_s = -inf.  With
+ * Sq == 1 every key is visible whatever `causal` says (the query sits at
+ * position Sk - 1). */
+int attn_fwd_splitkv(const void* q, const void* k, const void* v,
+                     float* o_accum, float* lse_accum, float* o, float* lse,
+                     int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal, float scale,
+                     int num_splits, void* stream);
+
+/* LSE-weighted combine of attn_fwd_splitkv's partials (forward-kernel page
+ * section 7.3): per row, LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s -
+ * LSE) O_s; splits with LSE_s = -inf weigh 0; a row whose splits are all -inf
+ * gets O = 0, LSE = -inf.  Writes o [B,Sq,Hq,d] and lse [B,Hq,Sq]. */
+int attn_splitkv_combine(const float* o_accum, const float* lse_accum, float* o, float* lse,
+                         int B, int Sq, int Hq, int d, int num_splits, void* stream);
+
+/* Static description of a status code. */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHFWD_H */

@@ -1,0 +1,80 @@
+// Device building blocks for the gfx950 attention kernels: vector types, the two
+// bf16 matrix-core instructions, 128-bit memory helpers, bf16 packing and
+// cross-lane reductions.  Wavefronts are 64 lanes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ff {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D(32x32) += A(32x16) * B(16x32).  Lane l supplies A[l%32][8*(l/32) .. +7] and
+// B[8*(l/32) .. +7][l%32]; it receives D[8*j + 4*(l/32) + i][l%32] in element
+// 4*j + i (j, i in 0..3).
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) * B(32x16).  Lane l supplies A[l%16][8*(l/16) .. +7] and
+// B[8*(l/16) .. +7][l%16]; it receives D[4*(l/16) + i][l%16] in element i.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two floats to packed bf16 (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ u32x4 pack8(float a0, float a1, float a2, float a3, float a4,
+                                       float a5, float a6, float a7) {
+  u32x4 r;
+  r[0] = pack_bf16(a0, a1);
+  r[1] = pack_bf16(a2, a3);
+  r[2] = pack_bf16(a4, a5);
+  r[3] = pack_bf16(a6, a7);
+  return r;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ void st16f(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_fmaxf(a, b); }
+
+// Low 16 bits of a and b packed (a in the low half); high halves likewise.
+__device__ __forceinline__ uint32_t lo_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// max over lanes l and l^32.
+__device__ __forceinline__ float max_xor32(float x) {
+  return vmax(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
+
+}  // namespace ff

@@ -1,0 +1,264 @@
+// libflashfwd: C-ABI entry points (declared in include/flashfwd.h).
+//
+// Host side of the attention forward path: argument checks, the tile and split
+// plans, and kernel launches on the caller's stream.  No allocation, no
+// synchronisation, no fallback: every step of the path runs in the kernels of
+// prefill.h and splitkv.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "flashfwd.h"
+#include "prefill.h"
+#include "splitkv.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+constexpr int kSplitRows = ff::SplitTraits<128>::BMD;  // folded rows per split workgroup
+constexpr int kSplitWgPerCu = 2;                        // resident split workgroups per CU
+constexpr int kMinBlocksPerSplit = 4;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (!a || !b) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Shape checks shared by the forward entry points.
+int check_dims(int B, int Sq, int Sk, int Hq, int Hkv, int d) {
+  if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1) return FF_ERR_SHAPE;
+  if (d != 64 && d != 128) return FF_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FF_ERR_GQA;
+  if ((int64_t)B * Sq * Hq * d >= kMaxElems || (int64_t)B * Sk * Hkv * d >= kMaxElems)
+    return FF_ERR_SHAPE;
+  return FF_OK;
+}
+
+int check_scale(float scale) {
+  if (!isfinite(scale) || !(scale > 0.f)) return FF_ERR_SCALE;
+  return FF_OK;
+}
+
+int check_io(const void* q, const void* k, const void* v, int B, int Sq, int Sk, int Hq,
+             int Hkv, int d, const void* const* outs, const int64_t* out_bytes, int nout) {
+  const int64_t qb = (int64_t)B * Sq * Hq * d * 2, kvb = (int64_t)B * Sk * Hkv * d * 2;
+  for (int i = 0; i < nout; ++i) {
+    if (overlaps(outs[i], out_bytes[i], q, qb) || overlaps(outs[i], out_bytes[i], k, kvb) ||
+        overlaps(outs[i], out_bytes[i], v, kvb))
+      return FF_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return FF_ERR_ALIAS;
+  }
+  return FF_OK;
+}
+
+std::atomic<int> g_cu_count[64];
+
+int device_cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FF_ERR_HIP;
+  if (dev >= 0 && dev < 64) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return FF_OK;
+    }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+    return FF_ERR_HIP;
+  if (dev >= 0 && dev < 64) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  *out = c;
+  return FF_OK;
+}
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? FF_OK : FF_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case FF_OK: return "ok";
+    case FF_ERR_NULL: return "a required pointer is NULL";
+    case FF_ERR_SHAPE: return "invalid or too large shape (B, Sq, Sk, Hq, Hkv)";
+    case FF_ERR_HEADDIM: return "head dimension must be 64 or 128";
+    case FF_ERR_GQA: return "Hq must be a multiple of Hkv";
+    case FF_ERR_ALIGN: return "pointers must be 16-byte aligned";
+    case FF_ERR_SPLITS: return "num_splits must be in [1, FF_MAX_SPLITS]";
+    case FF_ERR_SCALE: return "scale must be finite and positive";
+    case FF_ERR_HIP: return "HIP runtime error";
+    case FF_ERR_ALIAS: return "an output buffer overlaps another buffer";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Sq,
+             int Sk, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FF_ERR_NULL;
+  int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FF_ERR_ALIGN;
+  if ((st = check_scale(scale))) return st;
+  const void* outs[2] = {o, lse};
+  const int64_t ob[2] = {(int64_t)B * Sq * Hq * d * 4, (int64_t)B * Hq * Sq * 4};
+  if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 2))) return st;
+
+  ff::FwdParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.num_m = (int)cdiv(Sq, ff::PrefillTraits<128>::BM);
+  const int64_t total = (int64_t)p.num_m * B * Hq;
+  if (total >= kMaxElems) return FF_ERR_SHAPE;
+  p.total = (int)total;
+  p.scale_log2 = scale * ff::kLog2e;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)total), block(256);
+  if (d == 128) {
+    if (causal) hipLaunchKernelGGL((ff::attn_fwd_prefill<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ff::attn_fwd_prefill<128, false>), grid, block, 0, s, p);
+  } else {
+    if (causal) hipLaunchKernelGGL((ff::attn_fwd_prefill<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ff::attn_fwd_prefill<64, false>), grid, block, 0, s, p);
+  }
+  return launch_status();
+}
+
+int attn_splits_efficiency_rule(int units, int slots, int max_splits) {
+  if (units < 1 || slots < 1 || max_splits < 1) return -FF_ERR_SHAPE;
+  double best = 0.0;
+  for (int S = 1; S <= max_splits; ++S) {
+    const double w = (double)units * S / slots;
+    const double eff = w / ceil(w);
+    if (eff > best) best = eff;
+  }
+  for (int S = 1; S <= max_splits; ++S) {
+    const double w = (double)units * S / slots;
+    if (w / ceil(w) >= 0.85 * best) return S;
+  }
+  return 1;
+}
+
+int attn_splitkv_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int d, int num_cus) {
+  int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
+  if (st) return -st;
+  if (num_cus <= 0 && (st = device_cu_count(&num_cus))) return -st;
+  const int64_t rows = (int64_t)Sq * (Hq / Hkv);
+  const int64_t units = (int64_t)B * Hkv * cdiv(rows, kSplitRows);
+  const int64_t nblocks = cdiv(Sk, FF_SPLIT_BLOCK_N);
+  int64_t max_splits = nblocks / kMinBlocksPerSplit;
+  if (max_splits > FF_MAX_SPLITS) max_splits = FF_MAX_SPLITS;
+  if (max_splits < 1) max_splits = 1;
+  const int64_t slots = (int64_t)num_cus * kSplitWgPerCu;
+  if (units >= slots) return 1;
+  return attn_splits_efficiency_rule((int)units, (int)slots, (int)max_splits);
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o_accum,
+                     float* lse_accum, float* o, float* lse, int B, int Sq, int Sk, int Hq,
+                     int Hkv, int d, int causal, float scale, int num_splits, void* stream) {
+  if (!q || !k || !v) return FF_ERR_NULL;
+  if (num_splits < 1 || num_splits > FF_MAX_SPLITS) return FF_ERR_SPLITS;
+  if (num_splits == 1 && (!o || !lse)) return FF_ERR_NULL;
+  if (num_splits > 1 && (!o_accum || !lse_accum)) return FF_ERR_NULL;
+  int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return FF_ERR_ALIGN;
+  if (num_splits == 1 && (!aligned16(o) || !aligned16(lse))) return FF_ERR_ALIGN;
+  if (num_splits > 1 && (!aligned16(o_accum) || !aligned16(lse_accum))) return FF_ERR_ALIGN;
+  if ((st = check_scale(scale))) return st;
+  const int64_t rows_all = (int64_t)B * Hq * Sq;
+  if ((int64_t)num_splits * rows_all * d >= kMaxElems) return FF_ERR_SHAPE;
+  if (num_splits == 1) {
+    const void* outs[2] = {o, lse};
+    const int64_t ob[2] = {rows_all * d * 4, rows_all * 4};
+    if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 2))) return st;
+  } else {
+    const void* outs[2] = {o_accum, lse_accum};
+    const int64_t ob[2] = {num_splits * rows_all * d * 4, num_splits * rows_all * 4};
+    if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 2))) return st;
+  }
+
+  ff::SplitParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o_accum = o_accum;
+  p.lse_accum = lse_accum;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.rows = Sq * p.G;
+  p.num_mb = (int)cdiv(p.rows, kSplitRows);
+  p.num_splits = num_splits;
+  const int64_t nblocks = cdiv(Sk, FF_SPLIT_BLOCK_N);
+  p.split_keys = (int)(cdiv(nblocks, num_splits) * FF_SPLIT_BLOCK_N);
+  p.causal = (causal && Sq > 1) ? 1 : 0;
+  p.scale_log2 = scale * ff::kLog2e;
+  const int64_t total = (int64_t)B * Hkv * p.num_mb * num_splits;
+  if (total >= kMaxElems) return FF_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)total), block(256);
+  if (d == 128) hipLaunchKernelGGL(ff::attn_fwd_splitkv<128>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(ff::attn_fwd_splitkv<64>, grid, block, 0, s, p);
+  return launch_status();
+}
+
+int attn_splitkv_combine(const float* o_accum, const float* lse_accum, float* o, float* lse,
+                         int B, int Sq, int Hq, int d, int num_splits, void* stream) {
+  if (!o_accum || !lse_accum || !o || !lse) return FF_ERR_NULL;
+  if (B < 1 || Sq < 1 || Hq < 1) return FF_ERR_SHAPE;
+  if (d != 64 && d != 128) return FF_ERR_HEADDIM;
+  if (num_splits < 1 || num_splits > FF_MAX_SPLITS) return FF_ERR_SPLITS;
+  if (!aligned16(o_accum) || !aligned16(lse_accum) || !aligned16(o) || !aligned16(lse))
+    return FF_ERR_ALIGN;
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  if ((int64_t)num_splits * rows * d >= kMaxElems) return FF_ERR_SHAPE;
+  const int64_t ab = num_splits * rows * d * 4, lb = num_splits * rows * 4;
+  if (overlaps(o, rows * d * 4, o_accum, ab) || overlaps(o, rows * d * 4, lse_accum, lb) ||
+      overlaps(lse, rows * 4, o_accum, ab) || overlaps(lse, rows * 4, lse_accum, lb) ||
+      overlaps(o, rows * d * 4, lse, rows * 4))
+    return FF_ERR_ALIAS;
+  ff::CombineParams p;
+  p.o_accum = o_accum;
+  p.lse_accum = lse_accum;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Sq = Sq;
+  p.Hq = Hq;
+  p.num_splits = num_splits;
+  p.rows = (int)rows;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)cdiv(rows, 4)), block(256);
+  if (d == 128) hipLaunchKernelGGL(ff::attn_splitkv_combine<128>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(ff::attn_splitkv_combine<64>, grid, block, 0, s, p);
+  return launch_status();
+}
+
+}  // extern "C"

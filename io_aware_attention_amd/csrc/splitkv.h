@@ -1,0 +1,330 @@
+// attn_fwd_splitkv and attn_splitkv_combine: the split-KV forward pass for
+// short query blocks (decode), and the LSE-weighted combine of its partials
+// ("03 forward CUDA kernel", section 7; the walk-through's split-KV kernel and
+// grid description).
+//
+// A workgroup owns one (block of 16 folded query rows, batch, key/value head,
+// split).  The Hq/Hkv query heads that share a key/value head are folded into
+// the row dimension (row R -> query position R / G, head hk*G + R % G), so one
+// key/value stream serves the whole group (forward-kernel page section 7.4).
+// The split's key range is dealt to the 4 wavefronts in 32-key steps; each
+// wavefront keeps its own online-softmax state for the 16 rows and the four
+// states are merged through LDS at the end, exactly like the split combine.
+//
+// Products use v_mfma_f32_16x16x32_bf16:
+//   S^T (16 keys x 16 rows) = K . Q^T   A = K rows straight from global memory
+//   O^T (16 dcols x 16 rows) += V^T . P^T, 32 keys per instruction
+// The key rows of the two 16-key blocks are interleaved so that each lane's
+// eight scores are eight consecutive keys, which makes them the P^T operand
+// as they stand.  V goes through a per-wavefront LDS area, transposed on the
+// way in, so V^T fragments are single 128-bit LDS reads.
+#pragma once
+#include "device.h"
+
+namespace ff {
+
+struct SplitParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o_accum;
+  float* lse_accum;
+  float* o;
+  float* lse;
+  int B, Sq, Sk, Hq, Hkv, G;
+  int rows;         // Sq * G folded rows per key/value head
+  int num_mb;       // ceil(rows / 16)
+  int num_splits;
+  int split_keys;   // keys per split (a multiple of the split block)
+  int causal;
+  float scale_log2;
+};
+
+// Wavefront-local LDS handoff: the lanes of one wavefront exchange data through
+// LDS; the fences order the accesses and the wave barrier keeps the compiler
+// from moving them across each other.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D>
+struct SplitTraits {
+  static constexpr int BMD = 16;                  // folded rows per workgroup
+  static constexpr int TK = 32;                   // keys per wavefront step
+  static constexpr int kWaves = 4;
+  static constexpr int VS = TK * 2 + 16;          // V^T row stride in LDS, bytes
+  static constexpr int WV = D * VS;               // V^T area per wavefront
+  static constexpr int VB = TK * D / 8 / 4 / 64;  // 4-key x 8-dcol V blocks per lane
+  static constexpr int kCombine = kWaves * (2 * BMD + BMD * D) * 4;
+  static constexpr int kLds = kWaves * WV > kCombine ? kWaves * WV : kCombine;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_splitkv(SplitParams p) {
+  using T = SplitTraits<D>;
+  constexpr int TK = T::TK, VS = T::VS, VB = T::VB, NW = T::kWaves;
+  __shared__ __attribute__((aligned(16))) char smem[T::kLds];
+
+  int u = blockIdx.x;
+  const int s = u % p.num_splits;
+  u /= p.num_splits;
+  const int mb = u % p.num_mb;
+  u /= p.num_mb;
+  const int hk = u % p.Hkv;
+  const int b = u / p.Hkv;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int nr = lane & 15;   // row of this lane in the B operand and the outputs
+  const int g4 = lane >> 4;   // which 16-lane group
+
+  const int G = p.G, Sq = p.Sq, Sk = p.Sk;
+  const int R = mb * 16 + nr;
+  const bool row_ok = R < p.rows;
+  const int qi = R / G;
+  const int qh = hk * G + R % G;
+
+  // key range of this split, clipped by the causal limit of the block's last row
+  int j_lo = s * p.split_keys;
+  int j_hi = j_lo + p.split_keys < Sk ? j_lo + p.split_keys : Sk;
+  const int r_last = (mb * 16 + 16 < p.rows ? mb * 16 + 16 : p.rows) - 1;
+  const int i_first = (mb * 16) / G;
+  if (p.causal) {
+    const int lim = r_last / G + Sk - Sq + 1;
+    j_hi = lim < j_hi ? lim : j_hi;
+  }
+  // steps whose keys all lie below this bound need no element mask
+  const int nomask_end = p.causal ? (i_first + Sk - Sq + 1 < Sk ? i_first + Sk - Sq + 1 : Sk) : Sk;
+  const int row_lim = p.causal ? qi + Sk - Sq : 0x7fffffff;
+
+  const int64_t q_stride = (int64_t)p.Hq * D;
+  const int64_t kv_stride = (int64_t)p.Hkv * D;
+  const float c2 = p.scale_log2;
+
+  // Q^T fragments: Q[row][32c + 8 g4 .. +7]
+  u32x4 qf[D / 32];
+  {
+    const uint16_t* qp = p.q + ((int64_t)b * Sq + qi) * q_stride + (int64_t)qh * D + 8 * g4;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      if (row_ok) qf[c] = ld16(qp + 32 * c);
+      else qf[c] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  const uint16_t* kbase = p.k + (int64_t)b * Sk * kv_stride + (int64_t)hk * D;
+  const uint16_t* vbase = p.v + (int64_t)b * Sk * kv_stride + (int64_t)hk * D;
+  char* wv = smem + wave * T::WV;
+
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // K row read by this lane for key block kb: 8*(nr/4) + 4*kb + nr%4
+  const int krow0 = 8 * (nr >> 2) + (nr & 3);
+
+  for (int j0 = j_lo + wave * TK; j0 < j_hi; j0 += NW * TK) {
+    const bool partial = j0 + TK > Sk;
+    u32x4 kreg[2][D / 32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = j0 + krow0 + 4 * kb;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        if (!partial || key < Sk) kreg[kb][c] = ld16(kbase + (int64_t)key * kv_stride + 32 * c + 8 * g4);
+        else kreg[kb][c] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    u32x4 vreg[VB][4];
+#pragma unroll
+    for (int bi = 0; bi < VB; ++bi) {
+      const int blk = lane + 64 * bi;
+      const int cg = blk % (D / 8), kg = blk / (D / 8);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = j0 + 4 * kg + r;
+        if (!partial || key < Sk) vreg[bi][r] = ld16(vbase + (int64_t)key * kv_stride + 8 * cg);
+        else vreg[bi][r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // S^T = K . Q^T for the two 16-key blocks; lane element i is key j0 + 8 g4 + 4 kb + i
+    f32x4 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) sc[kb] = mfma16(kreg[kb][c], qf[c], sc[kb]);
+    }
+    if (j0 + TK > nomask_end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j0 + 8 * g4 + 4 * kb + i;
+          if (key >= Sk || key > row_lim) sc[kb][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = vmax(mx, sc[kb][i]);
+    mx = vmax(mx, __shfl_xor(mx, 16));
+    mx = vmax(mx, __shfl_xor(mx, 32));
+    const float m_new = vmax(m_run, mx * c2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pe = fast_exp2(__builtin_fmaf(sc[kb][i], c2, -m_use));
+        sc[kb][i] = pe;
+        ls += pe;
+      }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
+    const u32x4 pf = pack8(sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1],
+                           sc[1][2], sc[1][3]);
+    // V -> V^T in this wavefront's LDS area
+#pragma unroll
+    for (int bi = 0; bi < VB; ++bi) {
+      const int blk = lane + 64 * bi;
+      const int cg = blk % (D / 8), kg = blk / (D / 8);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int dw = c >> 1;
+        u32x2 val;
+        if (c & 1) {
+          val[0] = hi_hi(vreg[bi][0][dw], vreg[bi][1][dw]);
+          val[1] = hi_hi(vreg[bi][2][dw], vreg[bi][3][dw]);
+        } else {
+          val[0] = lo_lo(vreg[bi][0][dw], vreg[bi][1][dw]);
+          val[1] = lo_lo(vreg[bi][2][dw], vreg[bi][3][dw]);
+        }
+        *reinterpret_cast<u32x2*>(wv + (8 * cg + c) * VS + 8 * kg) = val;
+      }
+    }
+    wave_lds_sync();
+    // O^T += V^T . P^T; A operand: V^T[16 db + nr][8 g4 .. +7]
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(wv + (16 * db + nr) * VS + 16 * g4);
+      oacc[db] = mfma16(a, pf, oacc[db]);
+    }
+    wave_lds_sync();
+  }
+
+  // ---- merge the four wavefront states (same algebra as the split combine)
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  __syncthreads();
+  float* cm = reinterpret_cast<float*>(smem);
+  float* cl = cm + NW * 16;
+  float* co = cl + NW * 16;
+  if (g4 == 0) {
+    cm[wave * 16 + nr] = m_run;
+    cl[wave * 16 + nr] = l_tot;
+  }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+    st16f(co + (wave * 16 + nr) * D + 16 * db + 4 * g4, oacc[db]);
+  __syncthreads();
+
+  constexpr int DPT = D / 16;  // dcols per thread in the merge
+  const int row = tid >> 4;
+  const int dc0 = (tid & 15) * DPT;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = vmax(M, cm[w * 16 + row]);
+  float wgt[NW];
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    wgt[w] = (M == -INFINITY) ? 0.f : fast_exp2(cm[w * 16 + row] - M);
+    L += cl[w * 16 + row] * wgt[w];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float out[DPT];
+#pragma unroll
+  for (int c = 0; c < DPT; ++c) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc += co[(w * 16 + row) * D + dc0 + c] * wgt[w];
+    out[c] = acc * inv;
+  }
+  const float lse_val = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+
+  const int Ro = mb * 16 + row;
+  if (Ro < p.rows) {
+    const int i = Ro / G, h = hk * G + Ro % G;
+    float* dst;
+    float* ldst;
+    if (p.num_splits == 1) {
+      dst = p.o + ((int64_t)b * Sq + i) * q_stride + (int64_t)h * D + dc0;
+      ldst = p.lse + ((int64_t)b * p.Hq + h) * Sq + i;
+    } else {
+      const int64_t prow = (((int64_t)s * p.B + b) * p.Hq + h) * Sq + i;
+      dst = p.o_accum + prow * D + dc0;
+      ldst = p.lse_accum + prow;
+    }
+#pragma unroll
+    for (int c = 0; c < DPT; c += 4) st16f(dst + c, f32x4{out[c], out[c + 1], out[c + 2], out[c + 3]});
+    if ((tid & 15) == 0) *ldst = lse_val;
+  }
+}
+
+struct CombineParams {
+  const float* o_accum;
+  const float* lse_accum;
+  float* o;
+  float* lse;
+  int B, Sq, Hq, num_splits;
+  int rows;  // B * Hq * Sq
+};
+
+// One wavefront per (batch, head, query) row; lanes cover the head dimension.
+template <int D>
+__global__ __launch_bounds__(256) void attn_splitkv_combine(CombineParams p) {
+  constexpr int DPL = D / 64;  // dcols per lane
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= p.rows) return;
+  const int64_t split_stride = (int64_t)p.rows;
+  float M = -INFINITY;
+  for (int s = 0; s < p.num_splits; ++s) M = vmax(M, p.lse_accum[s * split_stride + row]);
+  const int i = row % p.Sq;
+  const int bh = row / p.Sq;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  float* orow = p.o + (((int64_t)b * p.Sq + i) * p.Hq + h) * D + lane * DPL;
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) orow[c] = 0.f;
+    if (lane == 0) p.lse[row] = -INFINITY;
+    return;
+  }
+  float sum = 0.f;
+  for (int s = 0; s < p.num_splits; ++s)
+    sum += fast_exp2((p.lse_accum[s * split_stride + row] - M) * kLog2e);
+  const float L = M + fast_log2(sum) * kLn2;
+  float acc[DPL];
+#pragma unroll
+  for (int c = 0; c < DPL; ++c) acc[c] = 0.f;
+  for (int s = 0; s < p.num_splits; ++s) {
+    const float w = fast_exp2((p.lse_accum[s * split_stride + row] - L) * kLog2e);
+    const float* src = p.o_accum + (s * split_stride + row) * D + lane * DPL;
+#pragma unroll
+    for (int c = 0; c < DPL; ++c) acc[c] += w * src[c];
+  }
+#pragma unroll
+  for (int c = 0; c < DPL; ++c) orow[c] = acc[c];
+  if (lane == 0) p.lse[row] = L;
+}
+
+}  // namespace ff

@@ -1,0 +1,153 @@
+"""ctypes binding for libflashfwd (include/flashfwd.h): same names, same arguments.
+
+Argument marshalling only -- every step of the attention path runs in the library's
+HIP kernels.  Tensor arguments may be torch tensors (their ``data_ptr()`` is passed) or
+raw integer device addresses; ``stream`` may be a torch stream, an integer hipStream_t or
+None (the null stream).  A non-zero status raises ``FlashFwdError``.  Loading fails loudly
+when the library has not been built: there is no other implementation to fall back to.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflashfwd.so")
+
+FF_OK = 0
+FF_MAX_SPLITS = 128
+FF_SPLIT_BLOCK_N = 128
+STATUS_NAMES = {0: "FF_OK", 1: "FF_ERR_NULL", 2: "FF_ERR_SHAPE", 3: "FF_ERR_HEADDIM",
+                4: "FF_ERR_GQA", 5: "FF_ERR_ALIGN", 6: "FF_ERR_SPLITS", 7: "FF_ERR_SCALE",
+                8: "FF_ERR_HIP", 9: "FF_ERR_ALIAS"}
+EXPORTS = ("attn_fwd", "attn_splitkv_num_splits", "attn_splits_efficiency_rule",
+           "attn_fwd_splitkv", "attn_splitkv_combine", "attn_status_string")
+
+
+class FlashFwdError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} "
+                         f"({status_string(status)})")
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load libflashfwd.so once; raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libflashfwd is not built ({path} missing); run "
+                          f"`python __graft_entry__.py build` or io_aware_attention_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+    lib.attn_splitkv_num_splits.argtypes = [I, I, I, I, I, I, I]
+    lib.attn_splits_efficiency_rule.argtypes = [I, I, I]
+    lib.attn_fwd_splitkv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.attn_splitkv_combine.argtypes = [P, P, P, P, I, I, I, I, I, P]
+    lib.attn_status_string.argtypes = [I]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    for name in EXPORTS[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(rc, where):
+    if rc != FF_OK:
+        raise FlashFwdError(rc, where)
+
+
+def status_string(status):
+    return load().attn_status_string(int(status)).decode()
+
+
+def attn_status_string(status):
+    return status_string(status)
+
+
+def attn_fwd(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream=None):
+    _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv,
+                           d, int(bool(causal)), float(scale), _stream(stream)), "attn_fwd")
+
+
+def attn_splitkv_num_splits(B, Sq, Sk, Hq, Hkv, d, num_cus=0):
+    r = load().attn_splitkv_num_splits(B, Sq, Sk, Hq, Hkv, d, num_cus)
+    if r < 1:
+        raise FlashFwdError(-r, "attn_splitkv_num_splits")
+    return r
+
+
+def attn_splits_efficiency_rule(units, slots, max_splits):
+    r = load().attn_splits_efficiency_rule(units, slots, max_splits)
+    if r < 1:
+        raise FlashFwdError(-r, "attn_splits_efficiency_rule")
+    return r
+
+
+def attn_fwd_splitkv(q, k, v, o_accum, lse_accum, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale,
+                     num_splits, stream=None):
+    _check(load().attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o_accum), _ptr(lse_accum),
+                                   _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, d, int(bool(causal)),
+                                   float(scale), int(num_splits), _stream(stream)),
+           "attn_fwd_splitkv")
+
+
+def attn_splitkv_combine(o_accum, lse_accum, o, lse, B, Sq, Hq, d, num_splits, stream=None):
+    _check(load().attn_splitkv_combine(_ptr(o_accum), _ptr(lse_accum), _ptr(o), _ptr(lse), B,
+                                       Sq, Hq, d, int(num_splits), _stream(stream)),
+           "attn_splitkv_combine")
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences: allocate outputs with torch, then call the entry points above.
+
+def forward(q, k, v, causal, scale, stream=None):
+    """O [B,Sq,Hq,d] fp32 and LSE [B,Hq,Sq] fp32 from bf16 q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d]."""
+    import torch
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream)
+    return o, lse
+
+
+def forward_splitkv(q, k, v, causal, scale, num_splits=0, stream=None, return_partials=False):
+    """Split-KV path: attn_fwd_splitkv then (num_splits > 1) attn_splitkv_combine.
+    num_splits = 0 takes attn_splitkv_num_splits' choice."""
+    import torch
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    if num_splits == 0:
+        num_splits = attn_splitkv_num_splits(B, Sq, Sk, Hq, Hkv, d)
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    if num_splits == 1:
+        attn_fwd_splitkv(q, k, v, None, None, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, 1,
+                         stream)
+        return (o, lse, None, None) if return_partials else (o, lse)
+    oa = torch.empty((num_splits, B, Hq, Sq, d), dtype=torch.float32, device=q.device)
+    la = torch.empty((num_splits, B, Hq, Sq), dtype=torch.float32, device=q.device)
+    attn_fwd_splitkv(q, k, v, oa, la, None, None, B, Sq, Sk, Hq, Hkv, d, causal, scale,
+                     num_splits, stream)
+    attn_splitkv_combine(oa, la, o, lse, B, Sq, Hq, d, num_splits, stream)
+    return (o, lse, oa, la) if return_partials else (o, lse)

@@ -1,0 +1,108 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, rejects bad
+arguments before touching the GPU, and its split-count rule reproduces the forward-kernel
+page's worked example.  No compute call is made here."""
+import json
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from io_aware_attention_amd import flashfwd as ff
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashfwd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\(", text, re.M)))
+
+
+def test_header_matches_binding():
+    assert declared_functions() == sorted(ff.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ff.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", ff.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings():
+    for code in range(10):
+        assert ff.status_string(code)
+    assert ff.status_string(0) == "ok"
+
+
+# Fake but aligned, distinct addresses: every call below must fail validation before any
+# HIP call is made, so they are never dereferenced.
+Q, K, V, O, L = 1 << 20, 2 << 30, 3 << 30, 4 << 32, 5 << 32
+GOOD = dict(B=1, Sq=8, Sk=8, Hq=2, Hkv=1, d=64, causal=0, scale=0.125)
+
+
+def call_fwd(q=Q, k=K, v=V, o=O, lse=L, **kw):
+    a = dict(GOOD, **kw)
+    return ff.load().attn_fwd(q, k, v, o, lse, a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hkv"], a["d"],
+                              a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(lse=None), 1),
+    (dict(B=0), 2), (dict(Sq=0), 2), (dict(Sk=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2),
+    (dict(d=96), 3), (dict(d=256), 3), (dict(Hq=3, Hkv=2), 4),
+    (dict(q=Q + 8), 5), (dict(o=O + 4), 5),
+    (dict(scale=0.0), 7), (dict(scale=-1.0), 7), (dict(scale=float("inf")), 7),
+    (dict(scale=float("nan")), 7),
+    (dict(o=Q), 9),
+    (dict(B=1 << 12, Sq=1 << 12, Hq=1 << 4, d=128), 2),
+])
+def test_attn_fwd_rejects(kw, code):
+    assert call_fwd(**kw) == code
+
+
+def test_splitkv_and_combine_reject():
+    lib = ff.load()
+    a = (1, 1, 300, 8, 2, 128, 0, 0.1)
+    assert lib.attn_fwd_splitkv(Q, K, V, None, None, O, L, *a, 0, None) == 6
+    assert lib.attn_fwd_splitkv(Q, K, V, None, None, O, L, *a, 129, None) == 6
+    assert lib.attn_fwd_splitkv(Q, K, V, None, None, O, L, *a, 2, None) == 1   # no accum
+    assert lib.attn_fwd_splitkv(Q, K, V, O, L, None, None, *a, 1, None) == 1   # no o/lse
+    assert lib.attn_fwd_splitkv(Q, K, V, O + 4, L, None, None, *a, 4, None) == 5
+    assert lib.attn_splitkv_combine(O, L, None, Q, 1, 1, 8, 128, 4, None) == 1
+    assert lib.attn_splitkv_combine(O, L, Q, K, 1, 1, 8, 96, 4, None) == 3
+    assert lib.attn_splitkv_combine(O, L, Q, K, 1, 1, 8, 128, 0, None) == 6
+    assert lib.attn_splitkv_combine(O, L, O, K, 1, 1, 8, 128, 4, None) == 9
+
+
+def test_efficiency_rule_reproduces_printed_example():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "split_heuristic_example.json")))
+    blocks, sms = g["blocks"], g["sms"]
+    for s, printed in g["printed_efficiency"].items():
+        w = blocks * int(s) / sms
+        assert round(w / math.ceil(w), 2) == printed
+    for max_splits in (3, 8, 64, 128):
+        assert ff.attn_splits_efficiency_rule(blocks, sms, max_splits) == g["printed_choice"]
+    assert ff.attn_splits_efficiency_rule(108, 108, 16) == 1
+    with pytest.raises(ff.FlashFwdError):
+        ff.attn_splits_efficiency_rule(0, 108, 4)
+
+
+def test_num_splits_retuned_for_256_cus():
+    # GQA decode, 8 x 8 (batch, kv-head) units of 4 folded rows on 256 CUs x 2 slots
+    s = ff.attn_splitkv_num_splits(8, 1, 32768, 32, 8, 128, 256)
+    units, slots = 64, 512
+    w = units * s / slots
+    assert w / math.ceil(w) >= 0.85 and 1 < s <= 64
+    # enough units to fill the GPU: no split
+    assert ff.attn_splitkv_num_splits(64, 1, 4096, 64, 8, 128, 256) == 1
+    # short key ranges keep at least 4 key blocks per split
+    assert ff.attn_splitkv_num_splits(1, 1, 4 * 128, 8, 8, 64, 256) == 1
+    assert ff.attn_splitkv_num_splits(1, 1, 8 * 128, 8, 8, 64, 256) <= 2
+    with pytest.raises(ff.FlashFwdError):
+        ff.attn_splitkv_num_splits(1, 1, 100, 3, 2, 64, 256)
