@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention forward path on one MI355X.
+
+A step is one call of the path over one batch of synthetic bf16 input already resident in
+HBM.  The headline line is the causal-prefill workload (B=4, Hq=Hkv=16, Sq=Sk=4096,
+d=128): ``value`` is its algorithmic TFLOP/s (4*d flops per visible query/key pair).  The
+same JSON line carries the split-KV GQA decode workload (K/V bytes per second over
+attn_fwd_splitkv + attn_splitkv_combine) and the other workloads, each with the
+roofline fraction of its dominant kernel, and the fp64 CPU oracle timed on this host's
+cores on a bounded sample of the headline workload.
+
+    python bench.py [--steps K] [--warmup W] [--workloads a,b] [--no-cpu-baseline]
+
+Progress goes to stderr; stdout gets exactly one JSON line.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "attn fwd TFLOP/s (bf16 causal prefill) + decode KV GB/s, % of roofline"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+HEADLINE = "causal_prefill"
+DECODE = "gqa_decode"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_prefill_causal_prefill_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_attention_amd", "csrc", f)
+                  for f in ("device.h", "prefill.h", "splitkv.h", "flashfwd.hip")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(Sq, Sk, causal):
+    if not causal:
+        return Sq * Sk
+    total = 0
+    for i in range(Sq):
+        total += max(0, min(Sk, i + Sk - Sq + 1))
+    return total
+
+
+def prefill_flops(w):
+    return 4 * w["d"] * visible_pairs(w["Sq"], w["Sk"], w["causal"]) * w["B"] * w["Hq"]
+
+
+def decode_bytes(w):
+    kv = 2 * w["B"] * w["Sk"] * w["Hkv"] * w["d"] * 2
+    q = w["B"] * w["Sq"] * w["Hq"] * w["d"] * 2
+    o = w["B"] * w["Sq"] * w["Hq"] * w["d"] * 4
+    lse = w["B"] * w["Hq"] * w["Sq"] * 4
+    return kv, q, o, lse
+
+
+def sources_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter summary, or
+    None when the summary is missing or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_sources_sha256") != sources_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record(self.stream)
+
+    def stop_ms(self):
+        self.b.record(self.stream)
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def to_dev(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def run_prefill(torch, ff, name, steps, warmup):
+    w = synth.WORKLOADS[name]
+    q, k, v = synth.make_qkv(w)
+    qd, kd, vd = (to_dev(torch, x) for x in (q, k, v))
+    B, Sq, Sk, Hq, Hkv, d = (w[x] for x in ("B", "Sq", "Sk", "Hq", "Hkv", "d"))
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ff.attn_fwd(qd, kd, vd, o, lse, B, Sq, Sk, Hq, Hkv, d, w["causal"], w["scale"], stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    wall0 = time.perf_counter()
+    t.start()
+    for _ in range(steps):
+        step()
+    ms = t.stop_ms() / steps
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3 / steps
+    assert torch.isfinite(o).all().item(), f"{name}: non-finite output"
+    flops = prefill_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    res = {
+        "workload": name, "metric": "TFLOP/s", "value": round(tflops, 2),
+        "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall_ms, 4),
+        "kernel": "attn_fwd_prefill", "algorithmic_flop_per_launch": flops,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
+    }
+    log(f"[bench] {name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of dense bf16 peak)")
+    return res, (q, k, v)
+
+
+def run_decode(torch, ff, name, steps, warmup):
+    w = synth.WORKLOADS[name]
+    q, k, v = synth.make_qkv(w)
+    qd, kd, vd = (to_dev(torch, x) for x in (q, k, v))
+    del k, v
+    B, Sq, Sk, Hq, Hkv, d = (w[x] for x in ("B", "Sq", "Sk", "Hq", "Hkv", "d"))
+    S = ff.attn_splitkv_num_splits(B, Sq, Sk, Hq, Hkv, d)
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda:0")
+    oa = torch.empty((S, B, Hq, Sq, d), dtype=torch.float32, device="cuda:0")
+    la = torch.empty((S, B, Hq, Sq), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+
+    def step(i=None):
+        if i is not None:
+            ev[i][0].record(stream)
+        if S == 1:
+            ff.attn_fwd_splitkv(qd, kd, vd, None, None, o, lse, B, Sq, Sk, Hq, Hkv, d,
+                                w["causal"], w["scale"], 1, stream)
+        else:
+            ff.attn_fwd_splitkv(qd, kd, vd, oa, la, None, None, B, Sq, Sk, Hq, Hkv, d,
+                                w["causal"], w["scale"], S, stream)
+        if i is not None:
+            ev[i][1].record(stream)
+        if S > 1:
+            ff.attn_splitkv_combine(oa, la, o, lse, B, Sq, Hq, d, S, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    t.start()
+    for i in range(steps):
+        step(i)
+    ms = t.stop_ms() / steps
+    torch.cuda.synchronize()
+    split_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    assert torch.isfinite(o).all().item(), f"{name}: non-finite output"
+    kvb, qb, ob, lb = decode_bytes(w)
+    step_gbs = (kvb + qb + ob + lb) / (ms * 1e-3) / 1e9
+    kern_bytes = kvb + qb
+    kern_gbs = kern_bytes / (split_ms * 1e-3) / 1e9
+    res = {
+        "workload": name, "metric": "GB/s", "value": round(step_gbs, 1),
+        "ms_per_step": round(ms, 4), "num_splits": S,
+        "kernel": "attn_fwd_splitkv", "kernel_ms": round(split_ms, 4),
+        "algorithmic_bytes_per_step": kvb + qb + ob + lb,
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(kern_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None},
+    }
+    log(f"[bench] {name}: {ms:.4f} ms/step (split-KV kernel {split_ms:.4f} ms, S={S}), "
+        f"{step_gbs:.0f} GB/s step, kernel {kern_gbs:.0f} GB/s "
+        f"({100 * kern_gbs / PEAK_HBM_GBS:.1f}% of HBM peak)")
+    return res
+
+
+def omp_threads():
+    try:
+        return int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+    except OSError:
+        return os.cpu_count()
+
+
+def cpu_baseline(name, inputs, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of rows of the workload."""
+    import oracle
+    w = synth.WORKLOADS[name]
+    q, k, v = inputs
+    orc = oracle.get()
+    B, Sq, Sk, Hq, d = (w[x] for x in ("B", "Sq", "Sk", "Hq", "d"))
+
+    def rows_for(n):
+        idx = np.linspace(0, B * Hq * Sq - 1, n).astype(np.int64)
+        return [(int(r // (Hq * Sq)), int((r // Sq) % Hq), int(r % Sq)) for r in idx]
+
+    def timed(rows):
+        t0 = time.perf_counter()
+        orc.rows(q, k, v, w["causal"], w["scale"], rows)
+        return time.perf_counter() - t0
+
+    pilot = rows_for(64)
+    per_row = timed(pilot) / len(pilot)
+    n = int(max(64, min(B * Hq * Sq, seconds / max(per_row, 1e-9))))
+    rows = rows_for(n)
+    secs = timed(rows)
+    vis = sum(max(0, min(Sk, i + Sk - Sq + 1)) if w["causal"] else Sk for _, _, i in rows)
+    flops = 4 * d * vis
+    tf = flops / secs / 1e12
+    log(f"[bench] cpu oracle: {n} rows in {secs:.1f} s on {omp_threads()} threads = "
+        f"{tf * 1e3:.3f} GFLOP/s (algorithmic)")
+    return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": omp_threads(), "kind": "oracle",
+            "sample": f"{n} of the {B * Hq * Sq} query rows of {name}, evenly spaced over "
+                      f"(batch, head, position); algorithmic flops of their visible keys; "
+                      f"{secs:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workloads", default="all",
+                    help="comma list of " + ",".join(synth.WORKLOADS) + " (default: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from io_aware_attention_amd import flashfwd as ff
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ff.load()
+
+    if args.copy_mib:
+        n = args.copy_mib << 20
+        x = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(args.steps):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": args.steps}), flush=True)
+        return
+
+    names = list(synth.WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
+    results = {}
+    headline_inputs = None
+    for name in names:
+        log(f"[bench] running {name} ...")
+        if name == DECODE:
+            results[name] = run_decode(torch, ff, name, args.steps, args.warmup)
+        else:
+            results[name], inputs = run_prefill(torch, ff, name, args.steps, args.warmup)
+            if name == HEADLINE:
+                headline_inputs = inputs
+        torch.cuda.empty_cache()
+
+    main_name = HEADLINE if HEADLINE in results else names[0]
+    main = results[main_name]
+    if main_name == HEADLINE:
+        traffic = measured_traffic()
+        main["roofline"]["traffic"] = traffic
+    cpu = None
+    if not args.no_cpu_baseline and headline_inputs is not None:
+        cpu = cpu_baseline(HEADLINE, headline_inputs, args.cpu_seconds)
+    w = synth.WORKLOADS[main_name]
+    line = {
+        "metric": METRIC,
+        "value": main["value"],
+        "unit": main["metric"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{main_name}: B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} "
+                               f"Sq={w['Sq']} Sk={w['Sk']} d={w['d']} "
+                               f"{'causal' if w['causal'] else 'non-causal'}",
+                   "B": w["B"], "Sq": w["Sq"], "Sk": w["Sk"], "Hq": w["Hq"], "Hkv": w["Hkv"],
+                   "d": w["d"], "causal": w["causal"], "parallelism": "none (1 GPU)"},
+        "roofline": main["roofline"],
+        "cpu_baseline": cpu,
+        "workloads": {k: v for k, v in results.items()},
+    }
+    if DECODE in results:
+        line["decode_kv_gbs"] = results[DECODE]["value"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
