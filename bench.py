@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "causal_prefill"
 DECODE = "gqa_decode"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_prefill_causal_prefill_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_attention_amd", "csrc", f)
                   for f in ("device.h", "prefill.h", "splitkv.h", "flashfwd.hip")]
 
@@ -72,13 +72,15 @@ def sources_digest():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the headline kernel from the committed counter summary, or
-    None when the summary is missing or the kernel sources changed since it was taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary
+    profiles/<kernel>_<workload>_traffic.txt, or None when the summary is missing or the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.lstrip().startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
@@ -296,9 +298,8 @@ def main():
 
     main_name = HEADLINE if HEADLINE in results else names[0]
     main = results[main_name]
-    if main_name == HEADLINE:
-        traffic = measured_traffic()
-        main["roofline"]["traffic"] = traffic
+    for name, res in results.items():
+        res["roofline"]["traffic"] = measured_traffic(res["kernel"], name)
     cpu = None
     if not args.no_cpu_baseline and headline_inputs is not None:
         cpu = cpu_baseline(HEADLINE, headline_inputs, args.cpu_seconds)
