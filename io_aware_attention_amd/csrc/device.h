@@ -70,10 +70,54 @@ __device__ __forceinline__ uint32_t hi_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// max over lanes l and l^32.
+// max over lanes l and l^32 (v_permlane32_swap exchanges the two wave halves).
 __device__ __forceinline__ float max_xor32(float x) {
-  return vmax(x, __shfl_xor(x, 32));
+  const uint32_t u = __float_as_uint(x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return vmax(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(p)));
+}
+
+// ds_read_b64_tr_b16 at LDS byte address a + OFF.  Within each group of 16 lanes,
+// result lane i, element j is element (i & 3) of the 8 bytes that lane 4j + (i >> 2)
+// addressed.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t a) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(uintptr_t)(a + OFF));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor (gfx9 layout: base, stride 0, num_records bytes, raw dword3).
+// Reads at byte offsets >= num_records return zero.
+__device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t num_records) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xffffu), (int)num_records,
+               0x00020000};
+}
+
+// 16 bytes per lane from buffer `desc` at byte offset voff straight into LDS at
+// lds_base + 16 * lane (buffer_load_dwordx4 ... lds; lds_base is wave-uniform).
+// Written as inline assembly: the compiler then neither tracks nor orders other LDS
+// reads behind these loads, so the caller must wait (vmcnt) and synchronise before
+// reading what they wrote.
+__device__ __forceinline__ void buffer_load_lds16(i32x4 desc, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(desc), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// All of this wave's vector-memory loads (including loads into LDS) have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
 

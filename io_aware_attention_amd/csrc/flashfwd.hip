@@ -131,6 +131,7 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, 
   const int64_t total = (int64_t)p.num_m * B * Hq;
   if (total >= kMaxElems) return FF_ERR_SHAPE;
   p.total = (int)total;
+  p.u_per = (int)cdiv((int64_t)B * Hkv, 8);
   p.scale_log2 = scale * ff::kLog2e;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);

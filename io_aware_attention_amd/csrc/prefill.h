@@ -31,6 +31,8 @@
 // the same up to rounding (the explainer's rescaling-invariance argument) while
 // the O rescale is skipped for almost every tile.
 #pragma once
+#include <utility>
+
 #include "device.h"
 
 namespace ff {
@@ -44,6 +46,7 @@ struct FwdParams {
   int B, Sq, Sk, Hq, Hkv, G;  // G = Hq / Hkv
   int num_m;                  // query tiles per (batch, head)
   int total;                  // num_m * B * Hq workgroups
+  int u_per;                  // (batch, kv head) units per XCD group: ceil(B * Hkv / 8)
   float scale_log2;           // scale * log2(e)
 };
 
@@ -65,8 +68,26 @@ struct MaskTag {
   static constexpr bool value = B;
 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, fully unrolled.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// The two transposing reads of GEMM1 fragment i = (db, kb, cp): keys
+// 32kb + 16cp + {0..3, 4..7} of the V tile, dcols 32db + lane's column.
+template <int I, int D, int ROWB>
+__device__ __forceinline__ void gemm1_read(uint32_t vbase, const int* va, u32x2& lo, u32x2& hi) {
+  constexpr int db = I / 4, kb = (I / 2) % 2, cp = I % 2;
+  constexpr int off = (32 * kb + 16 * cp) * ROWB;
+  const uint32_t a = vbase + va[db];
+  lo = ds_read_tr16_b64<off>(a);
+  hi = ds_read_tr16_b64<off + 4 * ROWB>(a);
+}
 
 template <int D>
 struct PrefillTraits {
@@ -92,14 +113,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   constexpr int LOADS = T::LOADS;
   __shared__ __attribute__((aligned(1024))) char smem[T::kLds];
 
-  // ---- which (batch, head, query tile) this workgroup owns
+  // ---- which (batch, head, query tile) this workgroup owns.  The work list is cut
+  // into groups of u_per (batch, kv head) units, one group per XCD; inside a group
+  // the order is query tile (heaviest first when causal), then unit, then query
+  // head of the unit, so each XCD starts its longest tiles first.
   const int idx = xcd_remap(blockIdx.x, p.total);
-  const int hg = idx % p.G;
-  const int t1 = idx / p.G;
-  const int mi = t1 % p.num_m;
-  const int t2 = t1 / p.num_m;
-  const int hk = t2 % p.Hkv;
-  const int b = t2 / p.Hkv;
+  const int U = p.B * p.Hkv;
+  const int grp = p.u_per * p.G * p.num_m;
+  const int sg = idx / grp;
+  const int r0 = idx - sg * grp;
+  const int n_units = (U - sg * p.u_per) < p.u_per ? (U - sg * p.u_per) : p.u_per;
+  const int mi = r0 / (n_units * p.G);
+  const int rest = r0 - mi * n_units * p.G;
+  const int unit = sg * p.u_per + rest / p.G;
+  const int hg = rest % p.G;
+  const int hk = unit % p.Hkv;
+  const int b = unit / p.Hkv;
   const int h = hk * p.G + hg;
   const int mblk = CAUSAL ? p.num_m - 1 - mi : mi;  // heaviest causal tiles first
   const int q0 = mblk * BM;
@@ -151,6 +180,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
       if (qrow < Sq) qf[c] = ld16(qp + 16 * c);
       else qf[c] = u32x4{0u, 0u, 0u, 0u};
     }
+    // Retire the Q loads here, visibly to the compiler, so that it does not wait on
+    // vector memory inside the key loop (where the K/V loads are in flight).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
 
   // ---- direct HBM -> LDS loads.  Wave w, load k fills the 1 KiB LDS block
@@ -166,20 +198,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     koff[k] = r * kv_row_bytes + 16 * (ph ^ T::kkey(r));
     voff[k] = r * kv_row_bytes + 16 * (ph ^ T::vkey(r));
   }
+  const uint32_t smem_addr = lds_addr(smem);
   auto issue_loads = [&](int t, int buf) {
     const int rows_left = Sk - t * BN;  // > 0 for every visited tile
     const uint32_t bytes = (uint32_t)rows_left * (uint32_t)kv_row_bytes;
     const int64_t toff = (int64_t)t * BN * kv_row_bytes;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + toff), 0, (int)bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + toff), 0, (int)bytes, 0x00020000);
-    char* kl = smem + buf * 2 * TILE + 1024 * LOADS * wave;
-    char* vl = kl + TILE;
+    const i32x4 rk = buffer_desc(kbase + toff, bytes);
+    const i32x4 rv = buffer_desc(vbase + toff, bytes);
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(smem_addr + buf * 2 * TILE + 1024 * LOADS * wave);
 #pragma unroll
     for (int k = 0; k < LOADS; ++k) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kl + 1024 * k), 16, koff[k], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vl + 1024 * k), 16, voff[k], 0, 0, 0);
+      buffer_load_lds16(rk, koff[k], kl + 1024 * k);
+      buffer_load_lds16(rv, voff[k], kl + TILE + 1024 * k);
     }
   };
 
@@ -271,20 +301,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
         pf[kb][cp] = pack8(sc[kb][8 * cp + 0], sc[kb][8 * cp + 1], sc[kb][8 * cp + 2],
                            sc[kb][8 * cp + 3], sc[kb][8 * cp + 4], sc[kb][8 * cp + 5],
                            sc[kb][8 * cp + 6], sc[kb][8 * cp + 7]);
-    // GEMM1: O^T += V^T . P^T, V^T fragments by two transposing reads
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int cp = 0; cp < 2; ++cp) {
-          const char* base = vl + va[db] + (32 * kb + 16 * cp) * ROWB;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + 4 * ROWB));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-          oacc[db] = mfma32(a, pf[kb][cp], oacc[db]);
-        }
+    // GEMM1: O^T += V^T . P^T.  Each V^T fragment is two transposing reads (keys
+    // +0..3 and +4..7); reads run two MFMAs ahead of their use.
+    constexpr int NG1 = (D / 32) * 4;  // MFMAs: (db, kb, cp)
+    const uint32_t vbase_addr = lds_addr(vl);
+    u32x2 flo[3], fhi[3];
+    gemm1_read<0, D, ROWB>(vbase_addr, va, flo[0], fhi[0]);
+    gemm1_read<1, D, ROWB>(vbase_addr, va, flo[1], fhi[1]);
+    static_for<NG1>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i + 2 < NG1) gemm1_read<i + 2, D, ROWB>(vbase_addr, va, flo[(i + 2) % 3], fhi[(i + 2) % 3]);
+      const u32x4 a = {flo[i % 3][0], flo[i % 3][1], fhi[i % 3][0], fhi[i % 3][1]};
+      constexpr int db = i / 4, kb = (i / 2) % 2, cp = i % 2;
+      oacc[db] = mfma32(a, pf[kb][cp], oacc[db]);
+    });
   };
 
   // ---- main loop: tiles n_max-1 down to 0, masked suffix first
@@ -296,20 +326,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     __syncthreads();
   }
   issue_loads(t, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's tile is in LDS
+  wait_vmem();  // this wave's share of the tile is in LDS
   __syncthreads();
   int buf = 0;
   for (; t >= 0 && t >= n_mask_lo; --t) {
     if (t > 0) issue_loads(t - 1, buf ^ 1);
     tile(t, buf, MaskTag<true>{});
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wait_vmem();
     __syncthreads();
     buf ^= 1;
   }
   for (; t >= 0; --t) {
     if (t > 0) issue_loads(t - 1, buf ^ 1);
     tile(t, buf, MaskTag<false>{});
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    wait_vmem();
     __syncthreads();
     buf ^= 1;
   }
