@@ -78,11 +78,12 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
 }
 
-// The two transposing reads of GEMM1 fragment i = (db, kb, cp): keys
+// The two transposing reads of GEMM1 fragment i = (kb, db, cp): keys
 // 32kb + 16cp + {0..3, 4..7} of the V tile, dcols 32db + lane's column.
 template <int I, int D, int ROWB>
 __device__ __forceinline__ void gemm1_read(uint32_t vbase, const int* va, u32x2& lo, u32x2& hi) {
-  constexpr int db = I / 4, kb = (I / 2) % 2, cp = I % 2;
+  constexpr int NG1 = (D / 32) * 4;  // key block major: (kb, db, cp)
+  constexpr int kb = I / (NG1 / 2), db = (I % (NG1 / 2)) / 2, cp = I % 2;
   constexpr int off = (32 * kb + 16 * cp) * ROWB;
   const uint32_t a = vbase + va[db];
   lo = ds_read_tr16_b64<off>(a);
@@ -97,7 +98,7 @@ struct PrefillTraits {
   static constexpr int ROWB = D * 2;               // bytes per K/V row in LDS
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int TILE = BN * ROWB;           // bytes per K or V tile
-  static constexpr int kLds = 2 * 2 * TILE;        // K and V, double buffered
+  static constexpr int kLds = 4 * TILE;            // K and V, double buffered each
   static constexpr int RPB = 256 / ROWB;           // rows per 256-byte bank line
   static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
   // swizzle keys: physical chunk = logical chunk ^ key(row)
@@ -198,20 +199,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     koff[k] = r * kv_row_bytes + 16 * (ph ^ T::kkey(r));
     voff[k] = r * kv_row_bytes + 16 * (ph ^ T::vkey(r));
   }
+  // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3; tile t uses parity t & 1.
   const uint32_t smem_addr = lds_addr(smem);
-  auto issue_loads = [&](int t, int buf) {
-    const int rows_left = Sk - t * BN;  // > 0 for every visited tile
+  auto kbuf = [&](int t) { return smem_addr + (t & 1) * TILE; };
+  auto vbuf = [&](int t) { return smem_addr + (2 + (t & 1)) * TILE; };
+  // Loads of tile t of K (or V) into its buffer.  A tile index below 0 gets an empty
+  // descriptor: every lane reads as out of range, and the buffer is not read later.
+  auto issue = [&](const char* base, const int* off, int t, uint32_t lds) {
+    const int rows_left = t >= 0 ? Sk - t * BN : 0;
     const uint32_t bytes = (uint32_t)rows_left * (uint32_t)kv_row_bytes;
-    const int64_t toff = (int64_t)t * BN * kv_row_bytes;
-    const i32x4 rk = buffer_desc(kbase + toff, bytes);
-    const i32x4 rv = buffer_desc(vbase + toff, bytes);
-    const uint32_t kl = __builtin_amdgcn_readfirstlane(smem_addr + buf * 2 * TILE + 1024 * LOADS * wave);
+    const int64_t toff = t >= 0 ? (int64_t)t * BN * kv_row_bytes : 0;
+    const i32x4 rd = buffer_desc(base + toff, bytes);
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds + 1024 * LOADS * wave);
 #pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
-      buffer_load_lds16(rk, koff[k], kl + 1024 * k);
-      buffer_load_lds16(rv, voff[k], kl + TILE + 1024 * k);
-    }
+    for (int k = 0; k < LOADS; ++k) buffer_load_lds16(rd, off[k], l0 + 1024 * k);
   };
+  auto issue_k = [&](int t) { issue(kbase, koff, t, kbuf(t)); };
+  auto issue_v = [&](int t) { issue(vbase, voff, t, vbuf(t)); };
 
   // ---- LDS read addresses
   // GEMM0 A operand: K row 32kb + prow (prow = n with bits 2 and 3 swapped),
@@ -238,43 +242,78 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   float m_run = -INFINITY;  // reference point, scale*log2(e) units
   float l_run = 0.f;        // running sum over this lane's keys
 
-  auto tile = [&](int t, int buf, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const char* kl = smem + buf * 2 * TILE;
-    const char* vl = kl + TILE;
-    // GEMM0: S^T for key blocks kb = 0, 1 (32 keys each)
-    f32x16 sc[2];
+  // GEMM0: S^T for key blocks kb = 0, 1 (32 keys each) of the K tile at `kl`.
+  auto gemm0 = [&](uint32_t kl, f32x16* sc) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) sc[kb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kl + ka[c] + kb * 32 * ROWB);
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(
+            (const __attribute__((address_space(3))) char*)(uintptr_t)(kl + ka[c] + kb * 32 * ROWB));
         sc[kb] = mfma32(a, qf[c], sc[kb]);
       }
-    }
-    // mask: element 4j+i of block kb is key t*BN + 32 kb + 16(j>>1) + 8H + 4(j&1) + i
-    if constexpr (MASKED) {
-      const int lim = CAUSAL ? qrow + Sk - Sq : 0x7fffffff;
+  };
+  // Element 4j+i of block kb is key t*BN + 32 kb + 16(j>>1) + 8H + 4(j&1) + i.
+  auto mask = [&](f32x16* sc, int t) {
+    const int lim = CAUSAL ? qrow + Sk - Sq : 0x7fffffff;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = t * BN + 32 * kb + 16 * (j >> 1) + 8 * H + 4 * (j & 1) + i;
-            if (key >= Sk || key > lim) sc[kb][4 * j + i] = -INFINITY;
-          }
-    }
-    // online softmax (base 2)
+        for (int i = 0; i < 4; ++i) {
+          const int key = t * BN + 32 * kb + 16 * (j >> 1) + 8 * H + 4 * (j & 1) + i;
+          if (key >= Sk || key > lim) sc[kb][4 * j + i] = -INFINITY;
+        }
+  };
+  // Row maximum of a score tile in scale*log2(e) units (both wave halves).
+  auto rowmax = [&](const f32x16* sc) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = vmax(mx, sc[kb][e]);
-    mx = max_xor32(mx) * c2;
+    return max_xor32(mx) * c2;
+  };
+  // ---- software-pipelined key loop, tiles n_max-1 down to 0.  While tile t's
+  // softmax and PV product run, tile t-1's QK^T product is issued (K streams one
+  // tile ahead of V) and its row maximum is taken in the shadow of tile t's PV
+  // product.  Masked tiles (key tail, causal diagonal) are the first ones visited.
+  int t = n_max - 1;
+  if ((t + 1) * BN > Sk) {
+    // key tail: rows past Sk must read as zeros even if the loads leave them alone
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < TILE / 16; i += T::kThreads) {
+      st16(smem + (t & 1) * TILE + 16 * i, z);
+      st16(smem + (2 + (t & 1)) * TILE + 16 * i, z);
+    }
+    __syncthreads();
+  }
+  issue_k(t);
+  issue_v(t);
+  issue_k(t - 1);
+  wait_vmem();  // this wave's share of the tiles is in LDS
+  __syncthreads();
+  f32x16 sc[2];
+  gemm0(kbuf(t), sc);
+  if (t >= n_mask_lo) mask(sc, t);
+  float mx = rowmax(sc);
+
+  // One step: softmax + PV of tile t; QK^T, mask and row max of tile t-1 if HAS_NEXT.
+  // The instruction order is fixed by hand: each group holds one MFMA, the LDS read
+  // two MFMAs ahead, and a share of the softmax VALU work, and sched_barrier(0)
+  // keeps the compiler from regrouping them (left alone it clusters the MFMAs and
+  // issues every LDS read just before its use).
+  constexpr int NG0 = 2 * (D / 16);  // GEMM0 MFMAs: (c, kb), kb fastest
+  constexpr int NG1 = 4 * (D / 32);  // GEMM1 MFMAs: (kb, db, cp)
+  auto step = [&](int t, auto has_next_tag, auto mask_next_tag) {
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
+    // reference point for tile t: raise it (and rescale o, l) only past the slack
     const bool raise = mx > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform: some row raises m
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
       const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;  // 0 when m_run = -inf
       m_run = raise ? mx : m_run;
       l_run *= alpha;
@@ -282,67 +321,92 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float ls = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(__builtin_fmaf(sc[kb][e], c2, -m_use));
-        sc[kb][e] = pe;
-        ls += pe;
-      }
-    l_run += ls;
-    // P^T fragments (GEMM1 B operand): elements 8c'..8c'+7 of block kb
+    if constexpr (HAS_NEXT) {
+      issue_v(t - 1);
+      issue_k(t - 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // -- block A: QK^T of tile t-1 interleaved with p = 2^(s c - m) of tile t
+    f32x16 sn[2];
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+    u32x4 kr[3];
+    const uint32_t kl = kbuf(t - 1);
+    auto kread = [&](int i) {
+      const int c = i >> 1, kb = i & 1;
+      return *reinterpret_cast<const u32x4*>(
+          (const __attribute__((address_space(3))) char*)(uintptr_t)(kl + ka[c] + kb * 32 * ROWB));
+    };
+    if constexpr (HAS_NEXT) {
+      kr[0] = kread(0);
+      kr[1] = kread(1);
+    }
+    float lsum[4] = {0.f, 0.f, 0.f, 0.f};
     u32x4 pf[2][2];
+    static_for<NG0>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (HAS_NEXT) {
+        if constexpr (i + 2 < NG0) kr[(i + 2) % 3] = kread(i + 2);
+        sn[i & 1] = mfma32(kr[i % 3], qf[i >> 1], sn[i & 1]);
+      }
+      constexpr int EPG = 32 / NG0;  // score elements per group
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int cp = 0; cp < 2; ++cp)
-        pf[kb][cp] = pack8(sc[kb][8 * cp + 0], sc[kb][8 * cp + 1], sc[kb][8 * cp + 2],
-                           sc[kb][8 * cp + 3], sc[kb][8 * cp + 4], sc[kb][8 * cp + 5],
-                           sc[kb][8 * cp + 6], sc[kb][8 * cp + 7]);
-    // GEMM1: O^T += V^T . P^T.  Each V^T fragment is two transposing reads (keys
-    // +0..3 and +4..7); reads run two MFMAs ahead of their use.
-    constexpr int NG1 = (D / 32) * 4;  // MFMAs: (db, kb, cp)
-    const uint32_t vbase_addr = lds_addr(vl);
+      for (int q = 0; q < EPG; ++q) {
+        const int e = i * EPG + q;  // 0..31: block e / 16, element e % 16
+        const float x = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], c2, -m_use));
+        sc[e >> 4][e & 15] = x;
+        lsum[q & 3] += x;
+      }
+      if constexpr (((i + 1) * EPG) % 8 == 0) {  // eight more probabilities: pack them
+        constexpr int e0 = (i + 1) * EPG - 8;
+        const f32x16& b = sc[e0 >> 4];
+        constexpr int o = e0 & 15;
+        pf[e0 >> 4][o >> 3] = pack8(b[o], b[o + 1], b[o + 2], b[o + 3], b[o + 4], b[o + 5], b[o + 6], b[o + 7]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+
+    // -- block B: PV of tile t interleaved with mask and row max of tile t-1
+    const uint32_t vl = vbuf(t);
     u32x2 flo[3], fhi[3];
-    gemm1_read<0, D, ROWB>(vbase_addr, va, flo[0], fhi[0]);
-    gemm1_read<1, D, ROWB>(vbase_addr, va, flo[1], fhi[1]);
+    gemm1_read<0, D, ROWB>(vl, va, flo[0], fhi[0]);
+    gemm1_read<1, D, ROWB>(vl, va, flo[1], fhi[1]);
+    const int lim = CAUSAL ? qrow + Sk - Sq : 0x7fffffff;
+    float mxn = -INFINITY;
     static_for<NG1>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      if constexpr (i + 2 < NG1) gemm1_read<i + 2, D, ROWB>(vbase_addr, va, flo[(i + 2) % 3], fhi[(i + 2) % 3]);
+      if constexpr (i + 2 < NG1) gemm1_read<i + 2, D, ROWB>(vl, va, flo[(i + 2) % 3], fhi[(i + 2) % 3]);
       const u32x4 a = {flo[i % 3][0], flo[i % 3][1], fhi[i % 3][0], fhi[i % 3][1]};
-      constexpr int db = i / 4, kb = (i / 2) % 2, cp = i % 2;
+      constexpr int kb = i / (NG1 / 2), db = (i % (NG1 / 2)) / 2, cp = i % 2;
       oacc[db] = mfma32(a, pf[kb][cp], oacc[db]);
+      if constexpr (HAS_NEXT) {
+        constexpr int EPG = 32 / NG1;
+#pragma unroll
+        for (int q = 0; q < EPG; ++q) {
+          const int e = i * EPG + q;
+          if constexpr (MASK_NEXT) {
+            const int j = (e & 15) >> 2, ii = e & 3;
+            const int key = (t - 1) * BN + 32 * (e >> 4) + 16 * (j >> 1) + 8 * H + 4 * (j & 1) + ii;
+            if (key >= Sk || key > lim) sn[e >> 4][e & 15] = -INFINITY;
+          }
+          mxn = vmax(mxn, sn[e >> 4][e & 15]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     });
+    if constexpr (HAS_NEXT) {
+      mx = max_xor32(mxn) * c2;
+      sc[0] = sn[0];
+      sc[1] = sn[1];
+      wait_vmem();
+      __syncthreads();
+    }
   };
-
-  // ---- main loop: tiles n_max-1 down to 0, masked suffix first
-  int t = n_max - 1;
-  if ((t + 1) * BN > Sk) {
-    // key tail: rows past Sk must read as zeros even if the loads leave them alone
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < 2 * TILE / 16; i += T::kThreads) st16(smem + 16 * i, z);
-    __syncthreads();
-  }
-  issue_loads(t, 0);
-  wait_vmem();  // this wave's share of the tile is in LDS
-  __syncthreads();
-  int buf = 0;
-  for (; t >= 0 && t >= n_mask_lo; --t) {
-    if (t > 0) issue_loads(t - 1, buf ^ 1);
-    tile(t, buf, MaskTag<true>{});
-    wait_vmem();
-    __syncthreads();
-    buf ^= 1;
-  }
-  for (; t >= 0; --t) {
-    if (t > 0) issue_loads(t - 1, buf ^ 1);
-    tile(t, buf, MaskTag<false>{});
-    wait_vmem();
-    __syncthreads();
-    buf ^= 1;
-  }
+  for (; t >= 1 && t - 1 >= n_mask_lo; --t) step(t, MaskTag<true>{}, MaskTag<true>{});
+  for (; t >= 1; --t) step(t, MaskTag<true>{}, MaskTag<false>{});
+  step(0, MaskTag<false>{}, MaskTag<false>{});
 
   // ---- epilogue: O = o / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + __shfl_xor(l_run, 32);
