@@ -32,6 +32,19 @@ class FlashFwdError(RuntimeError):
 _lib = None
 
 
+def _share_hip_runtime():
+    """Load torch's HIP runtime first, when torch is installed.
+
+    The library needs libamdhip64.so.7.  PyTorch ships its own copy with the same soname;
+    whichever copy is loaded first is the one the process uses.  Loading this library
+    before torch would put two HIP runtimes in the process, and device pointers from
+    torch would then be invalid in the library's runtime."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
 def load(path=LIB_PATH):
     """Load libflashfwd.so once; raises if it is missing."""
     global _lib
@@ -40,7 +53,8 @@ def load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"libflashfwd is not built ({path} missing); run "
                           f"`python __graft_entry__.py build` or io_aware_attention_amd/build.py")
-    lib = ctypes.CDLL(path)
+    _share_hip_runtime()
+    lib = ctypes.CDLL(os.path.abspath(path))
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
     lib.attn_splitkv_num_splits.argtypes = [I, I, I, I, I, I, I]

@@ -6,6 +6,7 @@ import math
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -106,3 +107,15 @@ def test_num_splits_retuned_for_256_cus():
     assert ff.attn_splitkv_num_splits(1, 1, 8 * 128, 8, 8, 64, 256) <= 2
     with pytest.raises(ff.FlashFwdError):
         ff.attn_splitkv_num_splits(1, 1, 100, 3, 2, 64, 256)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    # Loading the library first must not bring a second HIP runtime into the process.
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from io_aware_attention_amd import flashfwd; flashfwd.load()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "libs = {l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}\n"
+            "print(len(libs)); assert len(libs) == 1, libs\n") % ROOT
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
