@@ -199,10 +199,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     koff[k] = r * kv_row_bytes + 16 * (ph ^ T::kkey(r));
     voff[k] = r * kv_row_bytes + 16 * (ph ^ T::vkey(r));
   }
-  // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3; tile t uses parity t & 1.
+  // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3.  Tiles are visited from
+  // t = n_max - 1 down; tile t uses parity (n_max - 1 - t) & 1, so that the parity of
+  // each step of the twice-unrolled key loop is a compile-time constant.
   const uint32_t smem_addr = lds_addr(smem);
-  auto kbuf = [&](int t) { return smem_addr + (t & 1) * TILE; };
-  auto vbuf = [&](int t) { return smem_addr + (2 + (t & 1)) * TILE; };
+  auto par = [&](int t) { return (n_max - 1 - t) & 1; };
+  auto kbuf = [&](int t) { return smem_addr + par(t) * TILE; };
+  auto vbuf = [&](int t) { return smem_addr + (2 + par(t)) * TILE; };
   // Loads of tile t of K (or V) into its buffer.  A tile index below 0 gets an empty
   // descriptor: every lane reads as out of range, and the buffer is not read later.
   auto issue = [&](const char* base, const int* off, int t, uint32_t lds) {
@@ -255,18 +258,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
         sc[kb] = mfma32(a, qf[c], sc[kb]);
       }
   };
-  // Element 4j+i of block kb is key t*BN + 32 kb + 16(j>>1) + 8H + 4(j&1) + i.
+  // Score element e (block e / 16, accumulator index e % 16 = 4j + i) of tile t is
+  // key t*BN + 8H + key_off(e), key_off(e) = 32(e / 16) + 16(j >> 1) + 4(j & 1) + i.
+  // The key is visible to row qrow iff it is below Sk and (causal) at most
+  // qrow + Sk - Sq, that is iff key_off(e) <= vis_lim(t): one bound per tile against compile-time offsets.
+  auto key_off = [](int e) {
+    const int j = (e & 15) >> 2, i = e & 3;
+    return 32 * (e >> 4) + 16 * (j >> 1) + 4 * (j & 1) + i;
+  };
+  const int last_key = CAUSAL && qrow + Sk - Sq < Sk - 1 ? qrow + Sk - Sq : Sk - 1;
+  auto vis_lim = [&](int t) { return last_key - t * BN - 8 * H; };
   auto mask = [&](f32x16* sc, int t) {
-    const int lim = CAUSAL ? qrow + Sk - Sq : 0x7fffffff;
+    const int vl = vis_lim(t);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t * BN + 32 * kb + 16 * (j >> 1) + 8 * H + 4 * (j & 1) + i;
-          if (key >= Sk || key > lim) sc[kb][4 * j + i] = -INFINITY;
-        }
+    for (int e = 0; e < 32; ++e)
+      if (key_off(e) > vl) sc[e >> 4][e & 15] = -INFINITY;
   };
   // Row maximum of a score tile in scale*log2(e) units (both wave halves).
   auto rowmax = [&](const f32x16* sc) {
@@ -286,8 +292,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     // key tail: rows past Sk must read as zeros even if the loads leave them alone
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = tid; i < TILE / 16; i += T::kThreads) {
-      st16(smem + (t & 1) * TILE + 16 * i, z);
-      st16(smem + (2 + (t & 1)) * TILE + 16 * i, z);
+      st16(smem + 16 * i, z);  // parity 0: the first tile visited
+      st16(smem + 2 * TILE + 16 * i, z);
     }
     __syncthreads();
   }
@@ -296,21 +302,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   issue_k(t - 1);
   wait_vmem();  // this wave's share of the tiles is in LDS
   __syncthreads();
-  f32x16 sc[2];
-  gemm0(kbuf(t), sc);
-  if (t >= n_mask_lo) mask(sc, t);
-  float mx = rowmax(sc);
+  // Scores of two consecutive tiles: in a step of parity P, S[P] holds tile t's and
+  // S[P ^ 1] receives tile t-1's; the roles swap every step, so nothing is copied.
+  f32x16 S[2][2];
+  gemm0(kbuf(t), S[0]);
+  if (t >= n_mask_lo) mask(S[0], t);
+  float mx = rowmax(S[0]);
 
-  // One step: softmax + PV of tile t; QK^T, mask and row max of tile t-1 if HAS_NEXT.
+  // One step (parity P): softmax + PV of tile t; QK^T, mask and row max of tile t-1
+  // if HAS_NEXT.
   // The instruction order is fixed by hand: each group holds one MFMA, the LDS read
   // two MFMAs ahead, and a share of the softmax VALU work, and sched_barrier(0)
   // keeps the compiler from regrouping them (left alone it clusters the MFMAs and
   // issues every LDS read just before its use).
   constexpr int NG0 = 2 * (D / 16);  // GEMM0 MFMAs: (c, kb), kb fastest
   constexpr int NG1 = 4 * (D / 32);  // GEMM1 MFMAs: (kb, db, cp)
-  auto step = [&](int t, auto has_next_tag, auto mask_next_tag) {
+  auto step = [&](auto par_tag, int t, auto has_next_tag, auto mask_next_tag) {
+    constexpr int P = decltype(par_tag)::value;
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
+    f32x16(&sc)[2] = S[P];
+    f32x16(&sn)[2] = S[P ^ 1];
     // reference point for tile t: raise it (and rescale o, l) only past the slack
     const bool raise = mx > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
@@ -322,17 +334,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     if constexpr (HAS_NEXT) {
-      issue_v(t - 1);
-      issue_k(t - 2);
+      issue(vbase, voff, t - 1, smem_addr + (2 + (P ^ 1)) * TILE);
+      issue(kbase, koff, t - 2, smem_addr + P * TILE);
     }
     __builtin_amdgcn_sched_barrier(0);
 
     // -- block A: QK^T of tile t-1 interleaved with p = 2^(s c - m) of tile t
-    f32x16 sn[2];
     sn[0] = f32x16{};
     sn[1] = f32x16{};
     u32x4 kr[3];
-    const uint32_t kl = kbuf(t - 1);
+    const uint32_t kl = smem_addr + (P ^ 1) * TILE;  // K of tile t-1
     auto kread = [&](int i) {
       const int c = i >> 1, kb = i & 1;
       return *reinterpret_cast<const u32x4*>(
@@ -369,11 +380,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
     // -- block B: PV of tile t interleaved with mask and row max of tile t-1
-    const uint32_t vl = vbuf(t);
+    const uint32_t vl = smem_addr + (2 + P) * TILE;  // V of tile t
     u32x2 flo[3], fhi[3];
     gemm1_read<0, D, ROWB>(vl, va, flo[0], fhi[0]);
     gemm1_read<1, D, ROWB>(vl, va, flo[1], fhi[1]);
-    const int lim = CAUSAL ? qrow + Sk - Sq : 0x7fffffff;
+    const int vln = vis_lim(t - 1);
     float mxn = -INFINITY;
     static_for<NG1>([&](auto I) {
       constexpr int i = decltype(I)::value;
@@ -387,9 +398,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
         for (int q = 0; q < EPG; ++q) {
           const int e = i * EPG + q;
           if constexpr (MASK_NEXT) {
-            const int j = (e & 15) >> 2, ii = e & 3;
-            const int key = (t - 1) * BN + 32 * (e >> 4) + 16 * (j >> 1) + 8 * H + 4 * (j & 1) + ii;
-            if (key >= Sk || key > lim) sn[e >> 4][e & 15] = -INFINITY;
+            if (key_off(e) > vln) sn[e >> 4][e & 15] = -INFINITY;
           }
           mxn = vmax(mxn, sn[e >> 4][e & 15]);
         }
@@ -398,15 +407,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     });
     if constexpr (HAS_NEXT) {
       mx = max_xor32(mxn) * c2;
-      sc[0] = sn[0];
-      sc[1] = sn[1];
       wait_vmem();
       __syncthreads();
     }
   };
-  for (; t >= 1 && t - 1 >= n_mask_lo; --t) step(t, MaskTag<true>{}, MaskTag<true>{});
-  for (; t >= 1; --t) step(t, MaskTag<true>{}, MaskTag<false>{});
-  step(0, MaskTag<false>{}, MaskTag<false>{});
+  // The loop runs in pairs of steps (parity 0, then 1).  Masked tiles (key tail,
+  // causal diagonal) are the first ones visited: steps t with t - 1 >= n_mask_lo mask
+  // the next tile, and their number is rounded up to even (masking a tile that needs
+  // none changes nothing), so every pair loop starts at parity 0 and the mask code
+  // stays out of the main loop.
+  using Par0 = std::integral_constant<int, 0>;
+  using Par1 = std::integral_constant<int, 1>;
+  using Yes = MaskTag<true>;
+  using No = MaskTag<false>;
+  const int n_next = n_max - 1;  // steps that have a next tile
+  int n_masked = n_next - (n_mask_lo > 0 ? n_mask_lo : 0);
+  n_masked = n_masked < 0 ? 0 : (n_masked > n_next ? n_next : n_masked);
+  for (int pair = 0; pair < (n_masked + 1) / 2 && t >= 2; ++pair, t -= 2) {
+    step(Par0{}, t, Yes{}, Yes{});
+    step(Par1{}, t - 1, Yes{}, Yes{});
+  }
+  for (; t >= 2; t -= 2) {
+    step(Par0{}, t, Yes{}, No{});
+    step(Par1{}, t - 1, Yes{}, No{});
+  }
+  if (t == 1) {
+    step(Par0{}, 1, Yes{}, Yes{});
+    step(Par1{}, 0, No{}, No{});
+  } else {
+    step(Par0{}, 0, No{}, No{});
+  }
 
   // ---- epilogue: O = o / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + __shfl_xor(l_run, 32);
