@@ -76,7 +76,7 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
  * (section 7.2): the smallest split count whose wave efficiency is at least 85%
  * of the best, where efficiency(S) = w / ceil(w) and w = units * S / slots.
  * Here units = B * Hkv * ceil(Sq * (Hq/Hkv) / 16) workgroups per split and
- * slots = num_cus * 2 workgroups resident at once, and S is capped so every
+ * slots = num_cus (one split workgroup per CU), and S is capped so every
  * split keeps at least 4 key blocks of FF_SPLIT_BLOCK_N.  num_cus <= 0 queries
  * the current device.  Pure host arithmetic apart from that query.
  * Returns S >= 1, or the negated ff_status on invalid arguments. */

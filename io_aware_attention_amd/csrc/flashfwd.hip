@@ -18,7 +18,10 @@ namespace {
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
 constexpr int kSplitRows = ff::SplitTraits<128>::BMD;  // folded rows per split workgroup
-constexpr int kSplitWgPerCu = 2;                        // resident split workgroups per CU
+// Split workgroups counted per CU.  The split kernel keeps its next key step in
+// flight, so one workgroup streams at close to a CU's share of HBM bandwidth; a
+// second, partial round of workgroups costs more than it gains.
+constexpr int kSplitWgPerCu = 1;
 constexpr int kMinBlocksPerSplit = 4;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

@@ -62,7 +62,8 @@ struct SplitTraits {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_splitkv(SplitParams p) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist for the device target only
   using T = SplitTraits<D>;
   constexpr int TK = T::TK, VS = T::VS, VB = T::VB, NW = T::kWaves;
   __shared__ __attribute__((aligned(16))) char smem[T::kLds];
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void attn_fwd_splitkv(SplitParams p) {
   const int b = u / p.Hkv;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int nr = lane & 15;   // row of this lane in the B operand and the outputs
   const int g4 = lane >> 4;   // which 16-lane group
@@ -126,30 +127,35 @@ __global__ __launch_bounds__(256) void attn_fwd_splitkv(SplitParams p) {
   // K row read by this lane for key block kb: 8*(nr/4) + 4*kb + nr%4
   const int krow0 = 8 * (nr >> 2) + (nr & 3);
 
-  for (int j0 = j_lo + wave * TK; j0 < j_hi; j0 += NW * TK) {
-    const bool partial = j0 + TK > Sk;
-    u32x4 kreg[2][D / 32];
+  // Software pipeline: each wavefront's loads of its next 32-key step are in
+  // flight while the current step is computed (two register sets, swapped by
+  // unrolling the loop twice).
+  // Loads go through buffer descriptors that cover rows j0 .. min(j0 + TK, Sk) - 1
+  // of this key/value head, so rows past Sk read as zero without a branch.
+  const int kv_row_bytes = p.Hkv * D * 2;
+  auto load_kv = [&](int j0, u32x4 (&kreg)[2][D / 32], u32x4 (&vreg)[VB][4]) {
+    const int rows = Sk - j0 < TK ? Sk - j0 : TK;
+    const int nrec = rows > 0 ? rows * kv_row_bytes : 0;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (int64_t)j0 * kv_stride), (short)0, nrec, 0x00020000);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (int64_t)j0 * kv_stride), (short)0, nrec, 0x00020000);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = j0 + krow0 + 4 * kb;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        if (!partial || key < Sk) kreg[kb][c] = ld16(kbase + (int64_t)key * kv_stride + 32 * c + 8 * g4);
-        else kreg[kb][c] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    u32x4 vreg[VB][4];
+      for (int c = 0; c < D / 32; ++c)
+        kreg[kb][c] = __builtin_amdgcn_raw_buffer_load_b128(
+            rk, (krow0 + 4 * kb) * kv_row_bytes + (32 * c + 8 * g4) * 2, 0, 0);
 #pragma unroll
     for (int bi = 0; bi < VB; ++bi) {
       const int blk = lane + 64 * bi;
       const int cg = blk % (D / 8), kg = blk / (D / 8);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j0 + 4 * kg + r;
-        if (!partial || key < Sk) vreg[bi][r] = ld16(vbase + (int64_t)key * kv_stride + 8 * cg);
-        else vreg[bi][r] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int r = 0; r < 4; ++r)
+        vreg[bi][r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (4 * kg + r) * kv_row_bytes + 16 * cg, 0, 0);
     }
+  };
+  auto compute = [&](int j0, const u32x4 (&kreg)[2][D / 32], const u32x4 (&vreg)[VB][4]) {
     // S^T = K . Q^T for the two 16-key blocks; lane element i is key j0 + 8 g4 + 4 kb + i
     f32x4 sc[2];
 #pragma unroll
@@ -219,6 +225,26 @@ __global__ __launch_bounds__(256) void attn_fwd_splitkv(SplitParams p) {
       oacc[db] = mfma16(a, pf, oacc[db]);
     }
     wave_lds_sync();
+  };
+  // The prefetch is unconditional (a conditional one would make the compiler wait
+  // for it before the current step): past the split's end it re-reads the current
+  // step's rows, which the cache still holds.
+  u32x4 kA[2][D / 32], vA[VB][4], kB[2][D / 32], vB[VB][4];
+  int j0 = j_lo + wave * TK;
+  if (j0 < j_hi) {
+    load_kv(j0, kA, vA);
+    while (true) {
+      int j1 = j0 + NW * TK;
+      load_kv(j1 < j_hi ? j1 : j0, kB, vB);
+      compute(j0, kA, vA);
+      if (j1 >= j_hi) break;
+      j0 = j1;
+      j1 = j0 + NW * TK;
+      load_kv(j1 < j_hi ? j1 : j0, kA, vA);
+      compute(j0, kB, vB);
+      if (j1 >= j_hi) break;
+      j0 = j1;
+    }
   }
 
   // ---- merge the four wavefront states (same algebra as the split combine)
@@ -278,6 +304,7 @@ __global__ __launch_bounds__(256) void attn_fwd_splitkv(SplitParams p) {
     for (int c = 0; c < DPT; c += 4) st16f(dst + c, f32x4{out[c], out[c + 1], out[c + 2], out[c + 3]});
     if ((tid & 15) == 0) *ldst = lse_val;
   }
+#endif
 }
 
 struct CombineParams {

@@ -95,9 +95,10 @@ def test_efficiency_rule_reproduces_printed_example():
 
 
 def test_num_splits_retuned_for_256_cus():
-    # GQA decode, 8 x 8 (batch, kv-head) units of 4 folded rows on 256 CUs x 2 slots
+    # GQA decode, 8 x 8 (batch, kv-head) units of 4 folded rows on 256 CUs, one slot each
     s = ff.attn_splitkv_num_splits(8, 1, 32768, 32, 8, 128, 256)
-    units, slots = 64, 512
+    assert s == 4
+    units, slots = 64, 256
     w = units * s / slots
     assert w / math.ceil(w) >= 0.85 and 1 < s <= 64
     # enough units to fill the GPU: no split
