@@ -11,6 +11,12 @@ cores on a bounded sample of the headline workload.
 
     python bench.py [--steps K] [--warmup W] [--workloads a,b] [--no-cpu-baseline]
 
+Each workload runs W untimed warm-up steps, then exactly K steps between HIP events on
+the launch stream.  The default W = 300 is there for the clock: coming out of idle, the
+GPU needs about 30 ms of sustained load before its launch times settle (a causal_prefill
+launch takes ~315-360 us in the first milliseconds, ~283 us from ~30 ms on), so a short
+warm-up would time the ramp instead of the steady state.
+
 Progress goes to stderr; stdout gets exactly one JSON line.
 """
 import argparse
@@ -253,8 +259,8 @@ def cpu_baseline(name, inputs, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workloads", default="all",
                     help="comma list of " + ",".join(synth.WORKLOADS) + " (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
