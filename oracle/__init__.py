@@ -1,4 +1,4 @@
-"""CPU oracle for the attention forward pass -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the attention forward and backward passes -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
 may import this package.  The GPU library never loads it and it never loads the GPU
@@ -11,6 +11,9 @@ Functions (all return float64 numpy arrays):
   probs(q, k, v, causal, scale, b, h, i)  -> P [Sk]                           probability row
   online(q, k, v, causal, scale, blk)     -> (o, lse)                         per-row online loop
   split(q, k, v, causal, scale, blk, S)   -> (o_part, lse_part, o, lse)       split + combine
+  bwd(q, k, v, dout, causal, scale)       -> (dq, dk, dv, dsum, (dq_abs, dk_abs, dv_abs))
+                                             backward; dsum = D per row [B,Hq,Sq]; *_abs =
+                                             sums of absolute terms (for error bounds)
 
 Inputs are either float64 arrays or uint16 arrays holding bf16 bit patterns (widened
 exactly).  q is [B,Sq,Hq,d]; k and v are [B,Sk,Hkv,d].
@@ -52,8 +55,9 @@ class Oracle:
         lib.oracle_attn_probs.argtypes = _COMMON + [_I, _I, _I, _P]
         lib.oracle_attn_online.argtypes = _COMMON + [_I, _P, _P]
         lib.oracle_attn_split.argtypes = _COMMON + [_I, _I, _P, _P, _P, _P]
+        lib.oracle_attn_bwd.argtypes = _COMMON + [_P, _P, _P, _P, _P, _P, _P, _P]
         for f in ("oracle_attn_fwd", "oracle_attn_rows", "oracle_attn_probs",
-                  "oracle_attn_online", "oracle_attn_split"):
+                  "oracle_attn_online", "oracle_attn_split", "oracle_attn_bwd"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
 
@@ -128,6 +132,21 @@ class Oracle:
         self._ok(self.lib.oracle_attn_split(*a, int(blk), S, op.ctypes.data, lp.ctypes.data,
                                             o.ctypes.data, lse.ctypes.data), "split")
         return op, lp, o, lse
+
+    def bwd(self, q, k, v, dout, causal, scale):
+        arrs, (B, Sq, Sk, Hq, Hkv, d), a = self._args(q, k, v, causal, scale)
+        do_ = np.ascontiguousarray(dout)
+        if do_.dtype != arrs[0].dtype or do_.shape != arrs[0].shape:
+            raise ValueError("dout must match q in dtype and shape")
+        dq = np.zeros((B, Sq, Hq, d))
+        dk = np.zeros((B, Sk, Hkv, d))
+        dv = np.zeros((B, Sk, Hkv, d))
+        dsum = np.zeros((B, Hq, Sq))
+        dq_a, dk_a, dv_a = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+        self._ok(self.lib.oracle_attn_bwd(*a, do_.ctypes.data, dq.ctypes.data, dk.ctypes.data,
+                                          dv.ctypes.data, dsum.ctypes.data, dq_a.ctypes.data,
+                                          dk_a.ctypes.data, dv_a.ctypes.data), "bwd")
+        return dq, dk, dv, dsum, (dq_a, dk_a, dv_a)
 
 
 _default = None

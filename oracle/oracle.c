@@ -1,5 +1,5 @@
 /*
- * CPU oracle for the attention forward pass -- TEST INFRASTRUCTURE ONLY.
+ * CPU oracle for the attention forward and backward passes -- TEST INFRASTRUCTURE ONLY.
  *
  * Only tests, the smoke check and the benchmark's CPU-baseline leg may load this
  * code.  It shares nothing with the GPU library: no headers, no helpers, no
@@ -37,6 +37,16 @@
  *    each range yields (O_s, LSE_s) or (0, -inf) when empty; the combine takes
  *    LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s
  *    (forward-kernel page section 7.3).
+ *  - Backward (explainer, sections "backward: from the softmax derivative",
+ *    "training: backward recomputation" and "backward: back to Q, K, V"): with the
+ *    dense probability row P of the plain definition and the upstream gradient dO,
+ *      D    = sum_c dO_c O_c            (one scalar per row; equals sum_j P_j dP_j)
+ *      dP_j = <dO, v_j>
+ *      dS_j = P_j (dP_j - D)
+ *      dQ   = scale * sum_j dS_j k_j     dK_j += scale * dS_j q     dV_j += P_j dO
+ *    The scale enters dQ and dK as the 1/sqrt(d) of the page's table does.  Masked
+ *    keys have P = dS = 0; a row with no visible key contributes nothing.  With GQA,
+ *    dK and dV of a key/value head sum over the Hq/Hkv query heads that read it.
  */
 #include <math.h>
 #include <stdint.h>
@@ -339,6 +349,91 @@ int oracle_attn_split(int in_bf16, const void *q, const void *k, const void *v, 
     free(s);
     free(os);
     free(ls);
+  }
+  return 0;
+}
+
+/* Backward of the plain definition (see the header).  dout has q's layout and dtype
+ * convention.  dq [B,Sq,Hq,d], dk, dv [B,Sk,Hkv,d], dsum [B,Hq,Sq] (D per row).
+ * If dq_abs, dk_abs, dv_abs are non-NULL they receive, per element, the sum of the
+ * absolute values of the terms that make up dq, dk, dv:
+ *   scale * sum_j |dS_j| |k_jc|,  scale * sum_i |dS_ij| |q_ic|,  sum_i P_ij |dO_ic|.
+ * Work is split over (batch, key/value head) units, so dk and dv need no atomics. */
+int oracle_attn_bwd(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
+                    int Sk, int Hq, int Hkv, int d, int causal, double scale, const void *dout,
+                    double *dq, double *dk, double *dv, double *dsum, double *dq_abs,
+                    double *dk_abs, double *dv_abs) {
+  SETUP_PROBLEM
+  if (!dout || !dq || !dk || !dv || !dsum) return 1;
+  const int G = Hq / Hkv;
+  const int64_t nkv = (int64_t)B * Sk * Hkv * d;
+  for (int64_t x = 0; x < nkv; ++x) {
+    dk[x] = 0.0;
+    dv[x] = 0.0;
+    if (dk_abs) dk_abs[x] = 0.0;
+    if (dv_abs) dv_abs[x] = 0.0;
+  }
+  #pragma omp parallel
+  {
+    double *s = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+    double *prob = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+    double *ds = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
+    double *o_row = (double *)malloc(sizeof(double) * d);
+    #pragma omp for schedule(dynamic, 1)
+    for (int u = 0; u < B * Hkv; ++u) {
+      const int b = u / Hkv, hk = u % Hkv;
+      for (int h = hk * G; h < (hk + 1) * G; ++h) {
+        for (int i = 0; i < Sq; ++i) {
+          double lse;
+          oneshot_row(&P, b, h, i, s, prob, o_row, &lse);
+          /* D = sum_c dO_c O_c */
+          double dsum_i = 0.0;
+          for (int c = 0; c < d; ++c)
+            dsum_i += elem(dout, in_bf16, q_index(&P, b, i, h, c)) * o_row[c];
+          dsum[((int64_t)b * Hq + h) * Sq + i] = dsum_i;
+          /* dP_j = <dO, v_j>, dS_j = P_j (dP_j - D) */
+          for (int j = 0; j < Sk; ++j) {
+            if (prob[j] == 0.0) {
+              ds[j] = 0.0;
+              continue;
+            }
+            double dp = 0.0;
+            for (int c = 0; c < d; ++c)
+              dp += elem(dout, in_bf16, q_index(&P, b, i, h, c)) *
+                    elem(v, in_bf16, kv_index(&P, b, j, hk, c));
+            ds[j] = prob[j] * (dp - dsum_i);
+          }
+          /* dQ = scale sum_j dS_j k_j */
+          for (int c = 0; c < d; ++c) {
+            double acc = 0.0, acc_abs = 0.0;
+            for (int j = 0; j < Sk; ++j) {
+              const double kj = elem(k, in_bf16, kv_index(&P, b, j, hk, c));
+              acc += ds[j] * kj;
+              acc_abs += fabs(ds[j]) * fabs(kj);
+            }
+            dq[q_index(&P, b, i, h, c)] = scale * acc;
+            if (dq_abs) dq_abs[q_index(&P, b, i, h, c)] = scale * acc_abs;
+          }
+          /* dK_j += scale dS_j q,  dV_j += P_j dO */
+          for (int j = 0; j < Sk; ++j) {
+            if (prob[j] == 0.0) continue;
+            for (int c = 0; c < d; ++c) {
+              const int64_t x = kv_index(&P, b, j, hk, c);
+              const double qc = elem(q, in_bf16, q_index(&P, b, i, h, c));
+              const double doc = elem(dout, in_bf16, q_index(&P, b, i, h, c));
+              dk[x] += scale * ds[j] * qc;
+              dv[x] += prob[j] * doc;
+              if (dk_abs) dk_abs[x] += scale * fabs(ds[j]) * fabs(qc);
+              if (dv_abs) dv_abs[x] += prob[j] * fabs(doc);
+            }
+          }
+        }
+      }
+    }
+    free(s);
+    free(prob);
+    free(ds);
+    free(o_row);
   }
   return 0;
 }

@@ -322,12 +322,112 @@ def check_decimal_brute_force(orc):
             assert np.allclose(lse[fin], ld[fin], rtol=0, atol=TIGHT)
 
 
+# ---------------------------------------------------------------------------
+# Backward pass
+
+
+def check_backward_worked_example(orc):
+    g = golden("backward_examples.json")["worked"]
+    ks = [_num(x) for x in g["k"]]
+    q, k, v = one_row(g["q"], ks, g["v"])
+    do_ = np.full((1, 1, 1, 1), g["dO"])
+    dq, dk, dv, dsum, _ = orc.bwd(q, k, v, do_, False, g["scale"])
+    P = g["printed_P"]
+    assert abs(dsum[0, 0, 0] - g["printed_D"]) < TIGHT, dsum
+    # q = 1 and scale = 1: dK_j = dS_j exactly.
+    assert np.allclose(dk.ravel(), g["printed_dS"], rtol=0, atol=TIGHT), dk.ravel()
+    assert abs(sum(g["printed_dS"])) < TIGHT
+    assert np.allclose(dv.ravel(), [p * g["dO"] for p in P], rtol=0, atol=TIGHT), dv.ravel()
+    assert abs(dq[0, 0, 0, 0] - sum(x * kk for x, kk in zip(g["printed_dS"], ks))) < TIGHT
+    assert abs(g["dO"] * g["printed_O"] - g["printed_D"]) < TIGHT
+    # The same scores through the scale argument: k = [0, 1], scale = ln 3.  The scale
+    # enters both gradients: dQ = ln3 * (dS . k) = 1.5 ln3 again, dK = ln3 * dS * q.
+    q2, k2, v2 = one_row(g["q"], [0.0, 1.0], g["v"])
+    dq2, dk2, dv2, _, _ = orc.bwd(q2, k2, v2, do_, False, LN3)
+    assert abs(dq2[0, 0, 0, 0] - 1.5 * LN3) < TIGHT, dq2
+    assert np.allclose(dk2.ravel(), [LN3 * x for x in g["printed_dS"]], rtol=0, atol=TIGHT)
+    assert np.allclose(dv2, dv, rtol=0, atol=TIGHT)
+
+
+def check_backward_exercise_2(orc):
+    g = golden("backward_examples.json")["exercise_2"]
+    P, V, dO, want = g["P"], g["V"], g["dO"], g["derived"]
+    q, k, v = one_row([1.0], [math.log(x) for x in P], V)
+    do_ = np.full((1, 1, 1, 1), dO)
+    dq, dk, dv, dsum, _ = orc.bwd(q, k, v, do_, False, 1.0)
+    assert abs(dsum[0, 0, 0] - want["D"]) < TIGHT and abs(dO * want["O"] - want["D"]) < TIGHT
+    assert np.allclose(dk.ravel(), want["dS"], rtol=0, atol=TIGHT), dk.ravel()
+    assert np.allclose(dv.ravel(), want["dV"], rtol=0, atol=TIGHT), dv.ravel()
+    assert abs(sum(want["dS"])) < TIGHT   # the page's self-check
+
+
+def check_backward_finite_differences(orc):
+    # Independent pin: central differences of the forward oracle's loss <dO, O>
+    # (the explainer's CPU lab compares its gradients the same way).
+    h = 1e-5
+    for seed, (B, Sq, Sk, Hq, Hkv, d, causal, scale) in enumerate(
+            ((1, 3, 4, 2, 1, 3, False, 0.6), (1, 5, 3, 2, 2, 2, True, 0.9),
+             (2, 3, 6, 3, 1, 2, True, 0.45), (1, 4, 4, 1, 1, 4, True, 1.3))):
+        q, k, v = _rand(200 + seed, B, Sq, Sk, Hq, Hkv, d)
+        do_ = np.random.default_rng(300 + seed).standard_normal(q.shape)
+        dq, dk, dv, _, _ = orc.bwd(q, k, v, do_, causal, scale)
+
+        def loss(qq, kk, vv):
+            return float(np.sum(orc.fwd(qq, kk, vv, causal, scale)[0] * do_))
+
+        for which, grad in ((0, dq), (1, dk), (2, dv)):
+            base = [q, k, v]
+            for idx in np.ndindex(base[which].shape):
+                plus = [x.copy() for x in base]
+                minus = [x.copy() for x in base]
+                plus[which][idx] += h
+                minus[which][idx] -= h
+                fd = (loss(*plus) - loss(*minus)) / (2 * h)
+                assert abs(fd - grad[idx]) < 2e-8, (seed, which, idx, fd, grad[idx])
+
+
+def check_backward_invariants(orc):
+    for seed, (B, Sq, Sk, Hq, Hkv, d, causal) in enumerate(
+            ((2, 6, 9, 4, 2, 3, True), (1, 7, 5, 2, 1, 4, True), (2, 5, 5, 3, 3, 2, False))):
+        q, k, v = _rand(400 + seed, B, Sq, Sk, Hq, Hkv, d)
+        do_ = np.random.default_rng(500 + seed).standard_normal(q.shape)
+        scale = 0.7
+        dq, dk, dv, dsum, _ = orc.bwd(q, k, v, do_, causal, scale)
+        o, lse = orc.fwd(q, k, v, causal, scale)
+        # D is dO . O of the forward output.
+        assert np.allclose(dsum, np.einsum("bihc,bihc->bhi", do_, o), rtol=0, atol=TIGHT)
+        # Each row's dS sums to zero, so the keys' dK sum to zero per head and column.
+        assert np.allclose(dk.sum(axis=1), 0.0, rtol=0, atol=1e-11), dk.sum(axis=1)
+        # P rows sum to one (rows with a visible key), so the keys' dV sum to the
+        # group's dO over those rows.
+        seen = np.isfinite(lse)                                   # [B, Hq, Sq]
+        g = Hq // Hkv
+        want = np.einsum("bihc,bhi->bhc", do_, seen.astype(float)).reshape(B, Hkv, g, d).sum(2)
+        assert np.allclose(dv.sum(axis=1), want, rtol=0, atol=1e-11)
+        # A row with no visible key gets dQ = 0.
+        for b, h, i in zip(*np.nonzero(~seen)):
+            assert np.all(dq[b, i, h] == 0.0)
+
+
+def check_backward_bf16_widening(orc):
+    rng = np.random.default_rng(12)
+    shape_q, shape_kv = (1, 5, 2, 4), (1, 7, 1, 4)
+    bits = [(rng.integers(0, 2 ** 16, size=s, dtype=np.uint32) & 0x3F7F | 0x3C00).astype(np.uint16)
+            for s in (shape_q, shape_kv, shape_kv, shape_q)]
+    widened = [(b.astype(np.uint32) << 16).view(np.float32).astype(np.float64) for b in bits]
+    r1 = orc.bwd(*bits, True, 0.5)
+    r2 = orc.bwd(*widened, True, 0.5)
+    for a, b in zip(r1[:4], r2[:4]):
+        assert np.array_equal(a, b)
+
+
 ALL_CHECKS = [
     check_online_softmax_example, check_one_query_two_keys, check_exercise_1, check_exercise_2,
     check_causal_mask_pictures, check_tail_tile_case, check_special_cases,
     check_probability_rows, check_shift_invariance, check_key_permutation, check_gqa_grouping,
     check_online_and_split_agree, check_rows_match_full, check_bf16_widening,
-    check_decimal_brute_force,
+    check_decimal_brute_force, check_backward_worked_example, check_backward_exercise_2,
+    check_backward_finite_differences, check_backward_invariants, check_backward_bf16_widening,
 ]
 
 

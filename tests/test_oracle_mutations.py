@@ -1,6 +1,7 @@
 """Mutation tests: plant each mistake the explainer's CPU-lab section asks about into a
 copy of the oracle (dropping alpha on the old numerator, dropping the scale, turning the
-causal <= into <), rebuild it, and require at least one pin to fail."""
+causal <= into <), and a few plausible backward mistakes, rebuild it, and require at
+least one pin to fail."""
 import os
 
 import pytest
@@ -12,6 +13,13 @@ MUTANTS = {
     "drop_alpha_on_numerator": ("o_row[c] = alpha * o_row[c] + pv;", "o_row[c] = o_row[c] + pv;"),
     "drop_scale": ("return p->scale * acc;", "return acc;"),
     "causal_strict": ("return j <= i + p->Sk - p->Sq;", "return j < i + p->Sk - p->Sq;"),
+    # backward: the scale left out of dQ, D left out of dS, dS in place of P for dV,
+    # dK with the wrong sign
+    "bwd_drop_scale_dq": ("dq[q_index(&P, b, i, h, c)] = scale * acc;",
+                          "dq[q_index(&P, b, i, h, c)] = acc;"),
+    "bwd_ds_without_D": ("ds[j] = prob[j] * (dp - dsum_i);", "ds[j] = prob[j] * dp;"),
+    "bwd_dv_uses_ds": ("dv[x] += prob[j] * doc;", "dv[x] += ds[j] * doc;"),
+    "bwd_dk_sign": ("dk[x] += scale * ds[j] * qc;", "dk[x] -= scale * ds[j] * qc;"),
 }
 
 
