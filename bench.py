@@ -40,6 +40,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 fl
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "causal_prefill"
 DECODE = "gqa_decode"
+BACKWARD = "causal_prefill_bwd"   # attn_bwd over causal_prefill's inputs
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_attention_amd", "csrc", f)
                   for f in ("device.h", "prefill.h", "splitkv.h", "flashfwd.hip")]
@@ -157,6 +158,49 @@ def run_prefill(torch, ff, name, steps, warmup):
     return res, (q, k, v)
 
 
+def run_backward(torch, ff, steps, warmup):
+    """attn_bwd on causal_prefill's inputs: dO is tensor 3 of the workload's seed, O and LSE
+    come from attn_fwd.  A step is the three backward kernels (prep, dK/dV, dQ)."""
+    w = synth.WORKLOADS[HEADLINE]
+    q, k, v = synth.make_qkv(w)
+    dout = synth.normal_bf16(w["seed"], 3, q.shape)
+    qd, kd, vd, dod = (to_dev(torch, x) for x in (q, k, v, dout))
+    del q, k, v, dout
+    B, Sq, Sk, Hq, Hkv, d = (w[x] for x in ("B", "Sq", "Sk", "Hq", "Hkv", "d"))
+    o, lse = ff.forward(qd, kd, vd, w["causal"], w["scale"])
+    dq = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device="cuda:0")
+    dk = torch.empty((B, Sk, Hkv, d), dtype=torch.float32, device="cuda:0")
+    dv = torch.empty((B, Sk, Hkv, d), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(ff.attn_bwd_workspace_floats(B, Sq, Hq), dtype=torch.float32,
+                     device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ff.attn_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d,
+                    w["causal"], w["scale"], stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    t.start()
+    for _ in range(steps):
+        step()
+    ms = t.stop_ms() / steps
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(x).all().item() for x in (dq, dk, dv)), "non-finite gradient"
+    flops = 2.5 * prefill_flops(w)   # 10*d per visible pair: S, dP, dV, dQ, dK
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {BACKWARD}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of dense bf16 peak)")
+    return {"workload": BACKWARD, "metric": "TFLOP/s", "value": round(tflops, 2),
+            "ms_per_step": round(ms, 4), "kernel": "attn_bwd_dkdv",
+            "kernels": ["attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq"],
+            "algorithmic_flop_per_launch": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}}
+
+
 def run_decode(torch, ff, name, steps, warmup):
     w = synth.WORKLOADS[name]
     q, k, v = synth.make_qkv(w)
@@ -262,7 +306,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workloads", default="all",
-                    help="comma list of " + ",".join(synth.WORKLOADS) + " (default: all)")
+                    help="comma list of " + ",".join(list(synth.WORKLOADS) + [BACKWARD]) + " (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -289,13 +333,16 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": args.steps}), flush=True)
         return
 
-    names = list(synth.WORKLOADS) if args.workloads == "all" else args.workloads.split(",")
+    names = list(synth.WORKLOADS) + [BACKWARD] if args.workloads == "all" else \
+        args.workloads.split(",")
     results = {}
     headline_inputs = None
     for name in names:
         log(f"[bench] running {name} ...")
         if name == DECODE:
             results[name] = run_decode(torch, ff, name, args.steps, args.warmup)
+        elif name == BACKWARD:
+            results[name] = run_backward(torch, ff, args.steps, args.warmup)
         else:
             results[name], inputs = run_prefill(torch, ff, name, args.steps, args.warmup)
             if name == HEADLINE:
@@ -309,7 +356,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and headline_inputs is not None:
         cpu = cpu_baseline(HEADLINE, headline_inputs, args.cpu_seconds)
-    w = synth.WORKLOADS[main_name]
+    w = synth.WORKLOADS[main_name if main_name in synth.WORKLOADS else HEADLINE]
     line = {
         "metric": METRIC,
         "value": main["value"],

@@ -110,6 +110,31 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v,
 int attn_splitkv_combine(const float* o_accum, const float* lse_accum, float* o, float* lse,
                          int B, int Sq, int Hq, int d, int num_splits, void* stream);
 
+/* Size of attn_bwd's workspace, in floats: 2 * B * Hq * roundup(Sq, 64).  Returns the
+ * count, or the negated ff_status (FF_ERR_SHAPE) for B, Sq or Hq below 1. */
+long long attn_bwd_workspace_floats(int B, int Sq, int Hq);
+
+/* Backward of attn_fwd: dQ, dK, dV from the forward's saved LSE ("FlashAttention 1, 2, 3"
+ * explainer, sections "backward: from the softmax derivative", "training: backward
+ * recomputation" and "backward: back to Q, K, V").  P is recomputed as
+ * exp(scale * q.k - LSE), and with D = sum_c dO_c O_c per row:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ * Masked pairs (causal, bottom-right aligned as in attn_fwd) contribute nothing.  With
+ * GQA, dK and dV of a key/value head sum over its Hq/Hkv query heads.
+ *   q, k, v, dout: bf16, q and dout [B,Sq,Hq,d], k and v [B,Sk,Hkv,d]
+ *   o, lse: fp32 [B,Sq,Hq,d] and [B,Hq,Sq], as attn_fwd wrote them for the same inputs
+ *   dq: fp32 [B,Sq,Hq,d]; dk, dv: fp32 [B,Sk,Hkv,d]; all three written in full
+ *   ws: fp32 workspace of attn_bwd_workspace_floats(B, Sq, Hq) floats, owned by the
+ *       caller and overwritten (D and the LSE in base 2 per row; not part of the
+ *       interface after the call returns)
+ * P and dS are rounded to bf16 as matrix-core operands; all accumulation is fp32.  The
+ * result is bitwise deterministic (no atomics).  Argument rules and errors as for
+ * attn_fwd (dq, dk, dv and ws must not overlap each other or any input:
+ * FF_ERR_ALIAS).  Enqueues three kernels on `stream`. */
+int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, float* ws, int B, int Sq, int Sk,
+             int Hq, int Hkv, int d, int causal, float scale, void* stream);
+
 /* Static description of a status code. */
 const char* attn_status_string(int status);
 

@@ -1,0 +1,484 @@
+// attn_bwd: the backward pass of the fused attention forward, for gfx950.
+//
+// It follows the "FlashAttention 1, 2, 3" explainer's backward sections: P is not
+// stored but recomputed from the saved LSE, P = exp(scale * q.k - LSE); with the row
+// scalar D = sum_c dO_c O_c,
+//   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+// Masked pairs have P = dS = 0.  Three kernels, all deterministic (no atomics):
+//   attn_bwd_prep  D and the base-2 LSE per row (memory-bound, 16 lanes per row)
+//   attn_bwd_dq    one workgroup per 128-query tile, key/value tiles streamed
+//                  through LDS: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
+//   attn_bwd_dkdv  one workgroup per 128 keys of a key/value head, query tiles of
+//                  every query head of the group streamed through LDS:
+//                  S = Q K^T, dV^T += dO^T P, dP = dO V^T, dK^T += Q^T dS
+// The products use v_mfma_f32_32x32x16_bf16; P and dS are rounded to bf16 (RNE) as
+// MFMA operands, everything else stays fp32.  The dQ kernel is the forward kernel's
+// mirror image (key rows permuted so that scores are the next product's B operand);
+// the dK/dV kernel is the same with the roles of queries and keys exchanged.
+#pragma once
+#include "device.h"
+#include "prefill.h"
+
+namespace ff {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* o;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dsum;  // [B, Hq, sq_pad]  D per row
+  float* lse2;  // [B, Hq, sq_pad]  LSE * log2(e); +inf for rows with no visible key
+  int B, Sq, Sk, Hq, Hkv, G;
+  int sq_pad;        // Sq rounded up to 64: 256-byte aligned rows for the loads into LDS
+  int num_m;         // 128-query tiles per (batch, head)
+  int num_n;         // 128-key blocks per (batch, kv head)
+  float scale;       // softmax scale: enters dQ and dK
+  float scale_log2;  // scale * log2(e)
+};
+
+// ---- attn_bwd_prep: D = sum_c dO_c O_c and the base-2 LSE, one row per 16 lanes.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep(BwdParams p) {
+  constexpr int E = D / 16;  // columns per lane
+  const int rows = p.B * p.Hq * p.Sq;
+  const int r = blockIdx.x * 16 + (threadIdx.x >> 4);  // row in [B, Hq, Sq] order
+  const int sub = threadIdx.x & 15;
+  if (r >= rows) return;  // all 16 lanes of a row leave together
+  const int i = r % p.Sq, bh = r / p.Sq;
+  const int h = bh % p.Hq, b = bh / p.Hq;
+  const int64_t base = (((int64_t)b * p.Sq + i) * p.Hq + h) * D + sub * E;
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    acc += __uint_as_float((uint32_t)p.dout[base + e] << 16) * p.o[base + e];
+  acc += __shfl_xor(acc, 8);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 1);
+  if (sub == 0) {
+    const int64_t w = (int64_t)bh * p.sq_pad + i;
+    p.dsum[w] = acc;
+    const float l = p.lse[r];
+    p.lse2[w] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// Shared geometry of the two main kernels: 4 wavefronts of 32 rows, tiles of T rows
+// of the streamed tensors, row-major in LDS with the 16-byte chunks of each row
+// XOR-swizzled by swz(row).  The same swizzle serves the 128-bit row reads and the
+// transposing reads.
+template <int D, int TROWS>
+struct BwdTraits {
+  static constexpr int kThreads = 256;
+  static constexpr int ROWB = D * 2;                      // bytes per row in LDS
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per row
+  static constexpr int TILE = TROWS * ROWB;               // bytes per streamed tile
+  static constexpr int RPB = 256 / ROWB;                  // rows per 256-byte line
+  static constexpr int LOADS = TROWS * CPR / kThreads;    // 16-byte loads per thread per tile
+  static __device__ __forceinline__ int swz(int r) { return (r / RPB) % CPR; }
+};
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// 128-bit LDS read at byte address a.
+__device__ __forceinline__ u32x4 lds_b128(uint32_t a) {
+  return *reinterpret_cast<const u32x4*>((const __attribute__((address_space(3))) char*)(uintptr_t)a);
+}
+#endif
+
+// The transposing reads of one MFMA A operand: rows R + {0..3} (lo) and R + {4..7}
+// (hi) of a tile, through precomputed per-lane addresses; R is a multiple of 16, so
+// the swizzle of row R + r equals that of r and R enters as an immediate offset.
+template <int OFF>
+__device__ __forceinline__ u32x4 tr_operand(uint32_t base, uint32_t a_lo, uint32_t a_hi) {
+  const u32x2 lo = ds_read_tr16_b64<OFF>(base + a_lo);
+  const u32x2 hi = ds_read_tr16_b64<OFF>(base + a_hi);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Direct HBM -> LDS loads of one tile.  Wave w, load j fills the 1 KiB LDS block
+// LOADS*w + j: lane i writes chunk slot 64*(LOADS*w + j) + i, i.e. row slot/CPR,
+// physical chunk slot%CPR, which holds logical chunk (physical ^ swz(row)).  Rows at
+// or past `rows` are out of the descriptor's range and land as zeros.
+template <int LOADS>
+__device__ __forceinline__ void tile_load(const char* base, int rows, int row_bytes,
+                                          const int* off, uint32_t lds, int wave) {
+  const i32x4 rd = buffer_desc(base, rows > 0 ? (uint32_t)rows * (uint32_t)row_bytes : 0u);
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds + 1024 * LOADS * wave);
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) buffer_load_lds16(rd, off[j], l0 + 1024 * j);
+}
+
+// Per-lane addresses shared by both kernels (lane = 32 H + n, 16-lane group g, s).
+template <int D, int TROWS>
+struct BwdAddr {
+  using T = BwdTraits<D, TROWS>;
+  int row[D / 16];    // row read: tile row prow(n) (bits 2, 3 of n swapped), logical chunk 2c + H
+  int tlo[D / 32];    // transposing read, rows 8(g/2) + s/4, dcols 32db + 16(g%2) + 4(s%4)
+  int thi[D / 32];    // the same four rows further down
+  __device__ __forceinline__ BwdAddr(int lane) {
+    const int n = lane & 31, H = lane >> 5;
+    const int prow = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) row[c] = prow * T::ROWB + 16 * ((2 * c + H) ^ T::swz(prow));
+    const int g = lane >> 4, s = lane & 15;
+    const int vrow = 8 * (g >> 1) + (s >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int chunk = 4 * db + 2 * (g & 1) + ((s & 3) >> 1);
+      tlo[db] = vrow * T::ROWB + 16 * (chunk ^ T::swz(vrow)) + 8 * (s & 1);
+      thi[db] = (vrow + 4) * T::ROWB + 16 * (chunk ^ T::swz(vrow + 4)) + 8 * (s & 1);
+    }
+  }
+};
+
+// Score element e (accumulator index 4j + i) of a 32x32 product whose A rows were
+// read through prow: it belongs to row 16(j>>1) + 8H + 4(j&1) + i of the 32-row block.
+__device__ __forceinline__ constexpr int perm_row(int e) {
+  return 16 * ((e >> 2) >> 1) + 4 * ((e >> 2) & 1) + (e & 3);
+}
+
+// ---------------------------------------------------------------------------
+// attn_bwd_dq: one workgroup per (128-query tile, batch, query head).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq(BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist for the device target only
+  constexpr int BM = 128, BN = 64;
+  using T = BwdTraits<D, BN>;
+  constexpr int ROWB = T::ROWB, CPR = T::CPR, TILE = T::TILE, LOADS = T::LOADS;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K 0/1, V 2/3
+
+  const int total = p.num_m * p.B * p.Hq;
+  const int idx = xcd_remap(blockIdx.x, total);
+  const int bh = idx / p.num_m, mi = idx - bh * p.num_m;
+  const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.G;
+  const int mblk = CAUSAL ? p.num_m - 1 - mi : mi;  // heaviest causal tiles first
+  const int q0 = mblk * BM;
+  const int Sq = p.Sq, Sk = p.Sk;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31, H = lane >> 5;
+  const int qrow = q0 + wave * 32 + n;
+
+  // key tiles [0, n_max); tiles from n_mask need an element mask
+  const int nb_total = (Sk + BN - 1) / BN;
+  int n_max = nb_total;
+  if (CAUSAL) {
+    const int lim = (q0 + BM < Sq ? q0 + BM : Sq) - 1 + Sk - Sq;
+    n_max = lim < 0 ? 0 : ((lim / BN + 1) < n_max ? lim / BN + 1 : n_max);
+  }
+  int n_mask = (Sk % BN) ? nb_total - 1 : nb_total;
+  if (CAUSAL) {
+    const int first = q0 + Sk - Sq + 1;
+    const int tm = first <= 0 ? 0 : first / BN;
+    n_mask = tm < n_mask ? tm : n_mask;
+  }
+
+  const int64_t q_stride = (int64_t)p.Hq * D;
+  const int kv_row_bytes = p.Hkv * D * 2;
+  float* dq_row = p.dq + ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D;
+  if (n_max <= 0) {  // no visible key for any row of this tile: dQ = 0
+    if (qrow < Sq) {
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int c = H * 4; c < D; c += 8) st16f(dq_row + c, z);
+    }
+    return;
+  }
+
+  // resident Q^T and dO^T fragments: [qrow][16c + 8H .. +7]; this row's L2 and D
+  u32x4 qf[D / 16], of[D / 16];
+  float L2 = INFINITY, Dr = 0.f;
+  {
+    const int64_t off = ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D + 8 * H;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      qf[c] = qrow < Sq ? ld16(p.q + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      of[c] = qrow < Sq ? ld16(p.dout + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (qrow < Sq) {
+      const int64_t r = ((int64_t)b * p.Hq + h) * p.sq_pad + qrow;
+      L2 = p.lse2[r];
+      Dr = p.dsum[r];
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours in flight in the loop
+  }
+
+  const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)b * Sk * p.Hkv + hk) * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)b * Sk * p.Hkv + hk) * D * 2;
+  int loff[LOADS];
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j) {
+    const int slot = 64 * (LOADS * wave + j) + lane;
+    const int r = slot / CPR, ph = slot % CPR;
+    loff[j] = r * kv_row_bytes + 16 * (ph ^ T::swz(r));
+  }
+  const uint32_t smem_addr = lds_addr(smem);
+  auto issue = [&](int t) {
+    const int rows = Sk - t * BN;
+    const int64_t toff = (int64_t)t * BN * kv_row_bytes;
+    tile_load<LOADS>(kbase + toff, rows, kv_row_bytes, loff, smem_addr + (t & 1) * TILE, wave);
+    tile_load<LOADS>(vbase + toff, rows, kv_row_bytes, loff, smem_addr + (2 + (t & 1)) * TILE, wave);
+  };
+  const BwdAddr<D, BN> ad(lane);
+
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{};
+  const float c2 = p.scale_log2;
+  const int last_key = CAUSAL && qrow + Sk - Sq < Sk - 1 ? qrow + Sk - Sq : Sk - 1;
+
+  issue(0);
+  wait_vmem();
+  __syncthreads();
+  for (int t = 0; t < n_max; ++t) {
+    if (t + 1 < n_max) issue(t + 1);  // into the other buffers, free since the last barrier
+    const uint32_t kl = smem_addr + (t & 1) * TILE;
+    const uint32_t vl = smem_addr + (2 + (t & 1)) * TILE;
+    // S^T (keys x queries) = K Q^T and dP^T = V dO^T, two 32-key blocks
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        s[kb] = mfma32(lds_b128(kl + ad.row[c] + kb * 32 * ROWB), qf[c], s[kb]);
+        dp[kb] = mfma32(lds_b128(vl + ad.row[c] + kb * 32 * ROWB), of[c], dp[kb]);
+      }
+    }
+    // dS^T = P^T (dP^T - D) with P^T = 2^(s c2 - L2); masked keys give 0
+    const bool masked = t >= n_mask;
+    const int vis = last_key - t * BN - 8 * H;  // key offsets <= vis are visible
+    u32x4 dsf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float pr = fast_exp2(__builtin_fmaf(s[kb][e], c2, -L2));
+        if (masked && 32 * kb + perm_row(e) > vis) pr = 0.f;
+        ds[e] = pr * (dp[kb][e] - Dr);
+      }
+#pragma unroll
+      for (int cp = 0; cp < 2; ++cp)
+        dsf[kb][cp] = pack8(ds[8 * cp], ds[8 * cp + 1], ds[8 * cp + 2], ds[8 * cp + 3],
+                            ds[8 * cp + 4], ds[8 * cp + 5], ds[8 * cp + 6], ds[8 * cp + 7]);
+    }
+    // dQ^T (dcols x queries) += K^T dS^T; K^T through transposing reads of the K tile
+    static_for<2>([&](auto KB) {
+      constexpr int kb = decltype(KB)::value;
+      static_for<2>([&](auto CP) {
+        constexpr int cp = decltype(CP)::value;
+        constexpr int off = (32 * kb + 16 * cp) * ROWB;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          dqacc[db] = mfma32(tr_operand<off>(kl, ad.tlo[db], ad.thi[db]), dsf[kb][cp], dqacc[db]);
+      });
+    });
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // dQ = scale * dQ^T: element 4j + i of block db is dcol 32db + 8j + 4H + i
+  if (qrow < Sq) {
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 val = {dqacc[db][4 * j] * sc, dqacc[db][4 * j + 1] * sc,
+                           dqacc[db][4 * j + 2] * sc, dqacc[db][4 * j + 3] * sc};
+        st16f(dq_row + 32 * db + 8 * j + 4 * H, val);
+      }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// attn_bwd_dkdv: one workgroup per (128 keys, batch, key/value head); its query
+// tiles are those of every query head of the group.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(BwdParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BK = 128, BQ = 64;
+  using T = BwdTraits<D, BQ>;
+  constexpr int ROWB = T::ROWB, CPR = T::CPR, TILE = T::TILE, LOADS = T::LOADS;
+  // Q tiles 0/1, dO tiles 2/3, then L2 and D slots (1 KiB each: the 64 values use the
+  // first 256 bytes, the rest of the load lands as zeros)
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 4 * 1024];
+
+  const int total = p.num_n * p.B * p.Hkv;
+  const int idx = xcd_remap(blockIdx.x, total);
+  const int unit = idx / p.num_n, nb = idx - unit * p.num_n;  // low key blocks: most queries
+  const int b = unit / p.Hkv, hk = unit % p.Hkv;
+  const int k0 = nb * BK;
+  const int Sq = p.Sq, Sk = p.Sk;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31, H = lane >> 5;
+  const int key = k0 + wave * 32 + n;
+
+  // query tiles [qt_lo, num_qt) of each head; tiles below qt_mask need no mask
+  const int num_qt = (Sq + BQ - 1) / BQ;
+  int qt_lo = 0, qt_mask = 0;
+  if (CAUSAL) {
+    const int first_q = k0 - (Sk - Sq);  // first query that sees key k0
+    qt_lo = first_q <= 0 ? 0 : (first_q / BQ < num_qt ? first_q / BQ : num_qt);
+    // a tile needs a mask iff some key of the block lies past its first query's limit
+    const int q_full = k0 + BK - 1 - (Sk - Sq);  // queries >= q_full see every key of the block
+    qt_mask = q_full <= 0 ? 0 : (q_full + BQ - 1) / BQ;
+  }
+  const int per_head = num_qt - qt_lo;
+  const int items = per_head * p.G;
+
+  const int64_t kv_stride = (int64_t)p.Hkv * D;
+  const int q_row_bytes = p.Hq * D * 2;
+  float* dk_row = p.dk + ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D;
+  float* dv_row = p.dv + ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D;
+
+  // resident K and V fragments (B operands of S = Q K^T and dP = dO V^T)
+  u32x4 kf[D / 16], vf[D / 16];
+  {
+    const int64_t off = ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D + 8 * H;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      kf[c] = key < Sk ? ld16(p.k + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      vf[c] = key < Sk ? ld16(p.v + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
+
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    dkacc[i] = f32x16{};
+    dvacc[i] = f32x16{};
+  }
+
+  if (items > 0) {
+    int loff[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int slot = 64 * (LOADS * wave + j) + lane;
+      const int r = slot / CPR, ph = slot % CPR;
+      loff[j] = r * q_row_bytes + 16 * (ph ^ T::swz(r));
+    }
+    const uint32_t smem_addr = lds_addr(smem);
+    // item it: head h = hk*G + it / per_head, query tile qt_lo + it % per_head
+    auto issue = [&](int it) {
+      const int h = hk * p.G + it / per_head;
+      const int q0 = (qt_lo + it % per_head) * BQ;
+      const int64_t qoff = (((int64_t)b * Sq + q0) * p.Hq + h) * D * 2;
+      const int rows = Sq - q0;
+      const uint32_t par = it & 1;
+      tile_load<LOADS>(reinterpret_cast<const char*>(p.q) + qoff, rows, q_row_bytes, loff,
+                       smem_addr + par * TILE, wave);
+      tile_load<LOADS>(reinterpret_cast<const char*>(p.dout) + qoff, rows, q_row_bytes, loff,
+                       smem_addr + (2 + par) * TILE, wave);
+      if (wave < 2) {  // wave 0: L2, wave 1: D, 64 floats each
+        const float* src = (wave == 0 ? p.lse2 : p.dsum) + ((int64_t)b * p.Hq + h) * p.sq_pad + q0;
+        const int nv = rows < BQ ? rows : BQ;
+        const i32x4 rd = buffer_desc(src, (uint32_t)nv * 4u);
+        const uint32_t dst = smem_addr + 4 * TILE + (2 * wave + par) * 1024;
+        buffer_load_lds16(rd, 16 * lane, __builtin_amdgcn_readfirstlane(dst));
+      }
+    };
+    const BwdAddr<D, BQ> ad(lane);
+    const float c2 = p.scale_log2;
+
+    issue(0);
+    wait_vmem();
+    __syncthreads();
+    for (int it = 0; it < items; ++it) {
+      if (it + 1 < items) issue(it + 1);
+      const uint32_t par = it & 1;
+      const uint32_t ql = smem_addr + par * TILE;
+      const uint32_t ol = smem_addr + (2 + par) * TILE;
+      const uint32_t l2l = smem_addr + 4 * TILE + par * 1024;
+      const uint32_t dsl = smem_addr + 4 * TILE + (2 + par) * 1024;
+      const int qt = qt_lo + it % per_head;
+      const int q0 = qt * BQ;
+      const bool masked = CAUSAL && qt < qt_mask;
+      // key <= q + Sk - Sq  <=>  query offset in the tile >= key - (Sk - Sq) - q0
+      const int need = key - (Sk - Sq) - q0 - 8 * H;  // row offsets below need are masked
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // S (queries x keys) = Q K^T and dP = dO V^T for 32 queries
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          s = mfma32(lds_b128(ql + ad.row[c] + qb * 32 * ROWB), kf[c], s);
+          dp = mfma32(lds_b128(ol + ad.row[c] + qb * 32 * ROWB), vf[c], dp);
+        }
+        // L2 and D of this lane's 16 query rows: rows 32qb + 8H + {0..7} and +16
+        float l2[16], dd[16];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const uint32_t o = 4 * (32 * qb + 16 * half + 8 * H + 4 * w);
+            const u32x4 a = lds_b128(l2l + o), c = lds_b128(dsl + o);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              l2[8 * half + 4 * w + x] = __uint_as_float(a[x]);
+              dd[8 * half + 4 * w + x] = __uint_as_float(c[x]);
+            }
+          }
+        u32x4 pf[2], dsf[2];
+        float pr[16], ds[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float x = fast_exp2(__builtin_fmaf(s[e], c2, -l2[e]));
+          if (masked && 32 * qb + perm_row(e) < need) x = 0.f;
+          pr[e] = x;
+          ds[e] = x * (dp[e] - dd[e]);
+        }
+#pragma unroll
+        for (int cp = 0; cp < 2; ++cp) {
+          pf[cp] = pack8(pr[8 * cp], pr[8 * cp + 1], pr[8 * cp + 2], pr[8 * cp + 3],
+                         pr[8 * cp + 4], pr[8 * cp + 5], pr[8 * cp + 6], pr[8 * cp + 7]);
+          dsf[cp] = pack8(ds[8 * cp], ds[8 * cp + 1], ds[8 * cp + 2], ds[8 * cp + 3],
+                          ds[8 * cp + 4], ds[8 * cp + 5], ds[8 * cp + 6], ds[8 * cp + 7]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS through transposing reads
+        static_for<2>([&](auto CP) {
+          constexpr int cp = decltype(CP)::value;
+          const uint32_t rowoff = (32 * qb + 16 * cp) * ROWB;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            dvacc[db] = mfma32(tr_operand<0>(ol + rowoff, ad.tlo[db], ad.thi[db]), pf[cp], dvacc[db]);
+            dkacc[db] = mfma32(tr_operand<0>(ql + rowoff, ad.tlo[db], ad.thi[db]), dsf[cp], dkacc[db]);
+          }
+        });
+      }
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // dK = scale * dK^T, dV = dV^T: element 4j + i of block db is dcol 32db + 8j + 4H + i
+  if (key < Sk) {
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 32 * db + 8 * j + 4 * H;
+        st16f(dk_row + c, f32x4{dkacc[db][4 * j] * sc, dkacc[db][4 * j + 1] * sc,
+                                dkacc[db][4 * j + 2] * sc, dkacc[db][4 * j + 3] * sc});
+        st16f(dv_row + c, f32x4{dvacc[db][4 * j], dvacc[db][4 * j + 1], dvacc[db][4 * j + 2],
+                                dvacc[db][4 * j + 3]});
+      }
+  }
+#endif
+}
+
+}  // namespace ff

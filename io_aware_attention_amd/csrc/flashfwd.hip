@@ -13,6 +13,7 @@
 #include "flashfwd.h"
 #include "prefill.h"
 #include "splitkv.h"
+#include "backward.h"
 
 namespace {
 
@@ -104,6 +105,85 @@ const char* attn_status_string(int status) {
     case FF_ERR_ALIAS: return "an output buffer overlaps another buffer";
     default: return "unknown status";
   }
+}
+
+long long attn_bwd_workspace_floats(int B, int Sq, int Hq) {
+  if (B < 1 || Sq < 1 || Hq < 1) return -FF_ERR_SHAPE;
+  return 2LL * B * Hq * cdiv(Sq, 64) * 64;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, float* ws, int B, int Sq, int Sk,
+             int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws) return FF_ERR_NULL;
+  int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
+  if (st) return st;
+  const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, ws};
+  for (const void* x : ptrs)
+    if (!aligned16(x)) return FF_ERR_ALIGN;
+  if ((st = check_scale(scale))) return st;
+  const int64_t sq_pad = cdiv(Sq, 64) * 64;
+  const int64_t qf32 = (int64_t)B * Sq * Hq * d * 4, kvf32 = (int64_t)B * Sk * Hkv * d * 4;
+  const int64_t wsb = 2 * (int64_t)B * Hq * sq_pad * 4;
+  const void* outs[4] = {dq, dk, dv, ws};
+  const int64_t ob[4] = {qf32, kvf32, kvf32, wsb};
+  if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 4))) return st;
+  const int64_t in_b[3] = {qf32, (int64_t)B * Hq * Sq * 4, (int64_t)B * Sq * Hq * d * 2};
+  const void* ins[3] = {o, lse, dout};
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(outs[i], ob[i], ins[j], in_b[j])) return FF_ERR_ALIAS;
+
+  ff::BwdParams p;
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.dout = (const uint16_t*)dout;
+  p.o = o;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.dsum = ws;
+  p.lse2 = ws + (int64_t)B * Hq * sq_pad;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.sq_pad = (int)sq_pad;
+  p.num_m = (int)cdiv(Sq, 128);
+  p.num_n = (int)cdiv(Sk, 128);
+  if ((int64_t)p.num_m * B * Hq >= kMaxElems || (int64_t)p.num_n * B * Hkv >= kMaxElems)
+    return FF_ERR_SHAPE;
+  p.scale = scale;
+  p.scale_log2 = scale * ff::kLog2e;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 block(256);
+  const dim3 g_prep((unsigned)cdiv((int64_t)B * Hq * Sq, 16));
+  const dim3 g_dq((unsigned)((int64_t)p.num_m * B * Hq));
+  const dim3 g_dkdv((unsigned)((int64_t)p.num_n * B * Hkv));
+  if (d == 128) {
+    hipLaunchKernelGGL(ff::attn_bwd_prep<128>, g_prep, block, 0, s, p);
+    if (causal) {
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, true>), g_dkdv, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dq<128, true>), g_dq, block, 0, s, p);
+    } else {
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, false>), g_dkdv, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dq<128, false>), g_dq, block, 0, s, p);
+    }
+  } else {
+    hipLaunchKernelGGL(ff::attn_bwd_prep<64>, g_prep, block, 0, s, p);
+    if (causal) {
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, true>), g_dkdv, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dq<64, true>), g_dq, block, 0, s, p);
+    } else {
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, false>), g_dkdv, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dq<64, false>), g_dq, block, 0, s, p);
+    }
+  }
+  return launch_status();
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Sq,

@@ -19,7 +19,8 @@ STATUS_NAMES = {0: "FF_OK", 1: "FF_ERR_NULL", 2: "FF_ERR_SHAPE", 3: "FF_ERR_HEAD
                 4: "FF_ERR_GQA", 5: "FF_ERR_ALIGN", 6: "FF_ERR_SPLITS", 7: "FF_ERR_SCALE",
                 8: "FF_ERR_HIP", 9: "FF_ERR_ALIAS"}
 EXPORTS = ("attn_fwd", "attn_splitkv_num_splits", "attn_splits_efficiency_rule",
-           "attn_fwd_splitkv", "attn_splitkv_combine", "attn_status_string")
+           "attn_fwd_splitkv", "attn_splitkv_combine", "attn_bwd_workspace_floats", "attn_bwd",
+           "attn_status_string")
 
 
 class FlashFwdError(RuntimeError):
@@ -61,10 +62,13 @@ def load(path=LIB_PATH):
     lib.attn_splits_efficiency_rule.argtypes = [I, I, I]
     lib.attn_fwd_splitkv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.attn_splitkv_combine.argtypes = [P, P, P, P, I, I, I, I, I, P]
+    lib.attn_bwd_workspace_floats.argtypes = [I, I, I]
+    lib.attn_bwd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, P]
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
         getattr(lib, name).restype = ctypes.c_int
+    lib.attn_bwd_workspace_floats.restype = ctypes.c_longlong
     _lib = lib
     return lib
 
@@ -131,6 +135,20 @@ def attn_splitkv_combine(o_accum, lse_accum, o, lse, B, Sq, Hq, d, num_splits, s
            "attn_splitkv_combine")
 
 
+def attn_bwd_workspace_floats(B, Sq, Hq):
+    r = load().attn_bwd_workspace_floats(B, Sq, Hq)
+    if r < 0:
+        raise FlashFwdError(-r, "attn_bwd_workspace_floats")
+    return r
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causal, scale,
+             stream=None):
+    _check(load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(ws), B, Sq, Sk, Hq, Hkv, d, int(bool(causal)),
+                           float(scale), _stream(stream)), "attn_bwd")
+
+
 # ---------------------------------------------------------------------------
 # torch conveniences: allocate outputs with torch, then call the entry points above.
 
@@ -165,3 +183,17 @@ def forward_splitkv(q, k, v, causal, scale, num_splits=0, stream=None, return_pa
                      num_splits, stream)
     attn_splitkv_combine(oa, la, o, lse, B, Sq, Hq, d, num_splits, stream)
     return (o, lse, oa, la) if return_partials else (o, lse)
+
+
+def backward(q, k, v, o, lse, dout, causal, scale, stream=None):
+    """dq [B,Sq,Hq,d], dk and dv [B,Sk,Hkv,d] fp32 from bf16 q, k, v, dout and the fp32 o, lse
+    of the forward; the workspace is allocated here."""
+    import torch
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    dq = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, Sk, Hkv, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, Sk, Hkv, d), dtype=torch.float32, device=q.device)
+    ws = torch.empty(attn_bwd_workspace_floats(B, Sq, Hq), dtype=torch.float32, device=q.device)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream)
+    return dq, dk, dv

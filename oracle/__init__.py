@@ -11,7 +11,7 @@ Functions (all return float64 numpy arrays):
   probs(q, k, v, causal, scale, b, h, i)  -> P [Sk]                           probability row
   online(q, k, v, causal, scale, blk)     -> (o, lse)                         per-row online loop
   split(q, k, v, causal, scale, blk, S)   -> (o_part, lse_part, o, lse)       split + combine
-  bwd(q, k, v, dout, causal, scale)       -> (dq, dk, dv, dsum, (dq_abs, dk_abs, dv_abs))
+  bwd(q, k, v, dout, causal, scale[, units]) -> (dq, dk, dv, dsum, (dq_abs, dk_abs, dv_abs))
                                              backward; dsum = D per row [B,Hq,Sq]; *_abs =
                                              sums of absolute terms (for error bounds)
 
@@ -55,7 +55,7 @@ class Oracle:
         lib.oracle_attn_probs.argtypes = _COMMON + [_I, _I, _I, _P]
         lib.oracle_attn_online.argtypes = _COMMON + [_I, _P, _P]
         lib.oracle_attn_split.argtypes = _COMMON + [_I, _I, _P, _P, _P, _P]
-        lib.oracle_attn_bwd.argtypes = _COMMON + [_P, _P, _P, _P, _P, _P, _P, _P]
+        lib.oracle_attn_bwd.argtypes = _COMMON + [_P, _P, _P, _P, _P, _P, _P, _P, _P]
         for f in ("oracle_attn_fwd", "oracle_attn_rows", "oracle_attn_probs",
                   "oracle_attn_online", "oracle_attn_split", "oracle_attn_bwd"):
             getattr(lib, f).restype = ctypes.c_int
@@ -133,17 +133,26 @@ class Oracle:
                                             o.ctypes.data, lse.ctypes.data), "split")
         return op, lp, o, lse
 
-    def bwd(self, q, k, v, dout, causal, scale):
+    def bwd(self, q, k, v, dout, causal, scale, units=None):
+        """units: None (all) or an iterable of (b, hk) key/value units to compute; the
+        other units' slices of every output stay zero."""
         arrs, (B, Sq, Sk, Hq, Hkv, d), a = self._args(q, k, v, causal, scale)
         do_ = np.ascontiguousarray(dout)
         if do_.dtype != arrs[0].dtype or do_.shape != arrs[0].shape:
             raise ValueError("dout must match q in dtype and shape")
+        umask = None
+        if units is not None:
+            umask = np.zeros(B * Hkv, dtype=np.int32)
+            for b, hk in units:
+                umask[b * Hkv + hk] = 1
         dq = np.zeros((B, Sq, Hq, d))
         dk = np.zeros((B, Sk, Hkv, d))
         dv = np.zeros((B, Sk, Hkv, d))
         dsum = np.zeros((B, Hq, Sq))
         dq_a, dk_a, dv_a = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
-        self._ok(self.lib.oracle_attn_bwd(*a, do_.ctypes.data, dq.ctypes.data, dk.ctypes.data,
+        self._ok(self.lib.oracle_attn_bwd(*a, do_.ctypes.data,
+                                          None if umask is None else umask.ctypes.data,
+                                          dq.ctypes.data, dk.ctypes.data,
                                           dv.ctypes.data, dsum.ctypes.data, dq_a.ctypes.data,
                                           dk_a.ctypes.data, dv_a.ctypes.data), "bwd")
         return dq, dk, dv, dsum, (dq_a, dk_a, dv_a)

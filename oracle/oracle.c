@@ -358,82 +358,104 @@ int oracle_attn_split(int in_bf16, const void *q, const void *k, const void *v, 
  * If dq_abs, dk_abs, dv_abs are non-NULL they receive, per element, the sum of the
  * absolute values of the terms that make up dq, dk, dv:
  *   scale * sum_j |dS_j| |k_jc|,  scale * sum_i |dS_ij| |q_ic|,  sum_i P_ij |dO_ic|.
- * Work is split over (batch, key/value head) units, so dk and dv need no atomics. */
+ * units: NULL, or B*Hkv flags; only the (batch, key/value head) units with a non-zero
+ * flag are computed (their query heads' dq and dsum rows, their dk and dv), the rest of
+ * every output is zero.  Each unit is done in the two steps of the page's table: the
+ * full P and dS rows of its query heads (rows in parallel; dq and D on the way), then
+ * dV = P^T dO and dK = scale dS^T Q (keys in parallel). */
 int oracle_attn_bwd(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
                     int Sk, int Hq, int Hkv, int d, int causal, double scale, const void *dout,
-                    double *dq, double *dk, double *dv, double *dsum, double *dq_abs,
-                    double *dk_abs, double *dv_abs) {
+                    const int *units, double *dq, double *dk, double *dv, double *dsum,
+                    double *dq_abs, double *dk_abs, double *dv_abs) {
   SETUP_PROBLEM
   if (!dout || !dq || !dk || !dv || !dsum) return 1;
   const int G = Hq / Hkv;
-  const int64_t nkv = (int64_t)B * Sk * Hkv * d;
+  const int64_t nq = (int64_t)B * Sq * Hq * d, nkv = (int64_t)B * Sk * Hkv * d;
+  for (int64_t x = 0; x < nq; ++x) {
+    dq[x] = 0.0;
+    if (dq_abs) dq_abs[x] = 0.0;
+  }
+  for (int64_t x = 0; x < (int64_t)B * Hq * Sq; ++x) dsum[x] = 0.0;
   for (int64_t x = 0; x < nkv; ++x) {
     dk[x] = 0.0;
     dv[x] = 0.0;
     if (dk_abs) dk_abs[x] = 0.0;
     if (dv_abs) dv_abs[x] = 0.0;
   }
-  #pragma omp parallel
-  {
-    double *s = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
-    double *prob = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
-    double *ds = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
-    double *o_row = (double *)malloc(sizeof(double) * d);
-    #pragma omp for schedule(dynamic, 1)
-    for (int u = 0; u < B * Hkv; ++u) {
-      const int b = u / Hkv, hk = u % Hkv;
-      for (int h = hk * G; h < (hk + 1) * G; ++h) {
-        for (int i = 0; i < Sq; ++i) {
-          double lse;
-          oneshot_row(&P, b, h, i, s, prob, o_row, &lse);
-          /* D = sum_c dO_c O_c */
-          double dsum_i = 0.0;
+  const int64_t nrows = (int64_t)G * Sq;  /* query rows of one unit */
+  const int64_t rowlen = Sk > 0 ? Sk : 1;
+  double *p_all = (double *)malloc(sizeof(double) * nrows * rowlen);
+  double *ds_all = (double *)malloc(sizeof(double) * nrows * rowlen);
+  if (!p_all || !ds_all) {
+    free(p_all);
+    free(ds_all);
+    return 5;
+  }
+  for (int u = 0; u < B * Hkv; ++u) {
+    if (units && !units[u]) continue;
+    const int b = u / Hkv, hk = u % Hkv;
+    /* step 1: P and dS rows; D; dQ = scale sum_j dS_j k_j */
+    #pragma omp parallel
+    {
+      double *s = (double *)malloc(sizeof(double) * rowlen);
+      double *o_row = (double *)malloc(sizeof(double) * d);
+      #pragma omp for schedule(dynamic, 4)
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int h = hk * G + (int)(r / Sq), i = (int)(r % Sq);
+        double *prob = p_all + r * rowlen, *ds = ds_all + r * rowlen;
+        double lse;
+        oneshot_row(&P, b, h, i, s, prob, o_row, &lse);
+        /* D = sum_c dO_c O_c */
+        double dsum_i = 0.0;
+        for (int c = 0; c < d; ++c)
+          dsum_i += elem(dout, in_bf16, q_index(&P, b, i, h, c)) * o_row[c];
+        dsum[((int64_t)b * Hq + h) * Sq + i] = dsum_i;
+        /* dP_j = <dO, v_j>, dS_j = P_j (dP_j - D) */
+        for (int j = 0; j < Sk; ++j) {
+          if (prob[j] == 0.0) {
+            ds[j] = 0.0;
+            continue;
+          }
+          double dp = 0.0;
           for (int c = 0; c < d; ++c)
-            dsum_i += elem(dout, in_bf16, q_index(&P, b, i, h, c)) * o_row[c];
-          dsum[((int64_t)b * Hq + h) * Sq + i] = dsum_i;
-          /* dP_j = <dO, v_j>, dS_j = P_j (dP_j - D) */
+            dp += elem(dout, in_bf16, q_index(&P, b, i, h, c)) *
+                  elem(v, in_bf16, kv_index(&P, b, j, hk, c));
+          ds[j] = prob[j] * (dp - dsum_i);
+        }
+        for (int c = 0; c < d; ++c) {
+          double acc = 0.0, acc_abs = 0.0;
           for (int j = 0; j < Sk; ++j) {
-            if (prob[j] == 0.0) {
-              ds[j] = 0.0;
-              continue;
-            }
-            double dp = 0.0;
-            for (int c = 0; c < d; ++c)
-              dp += elem(dout, in_bf16, q_index(&P, b, i, h, c)) *
-                    elem(v, in_bf16, kv_index(&P, b, j, hk, c));
-            ds[j] = prob[j] * (dp - dsum_i);
+            const double kj = elem(k, in_bf16, kv_index(&P, b, j, hk, c));
+            acc += ds[j] * kj;
+            acc_abs += fabs(ds[j]) * fabs(kj);
           }
-          /* dQ = scale sum_j dS_j k_j */
-          for (int c = 0; c < d; ++c) {
-            double acc = 0.0, acc_abs = 0.0;
-            for (int j = 0; j < Sk; ++j) {
-              const double kj = elem(k, in_bf16, kv_index(&P, b, j, hk, c));
-              acc += ds[j] * kj;
-              acc_abs += fabs(ds[j]) * fabs(kj);
-            }
-            dq[q_index(&P, b, i, h, c)] = scale * acc;
-            if (dq_abs) dq_abs[q_index(&P, b, i, h, c)] = scale * acc_abs;
-          }
-          /* dK_j += scale dS_j q,  dV_j += P_j dO */
-          for (int j = 0; j < Sk; ++j) {
-            if (prob[j] == 0.0) continue;
-            for (int c = 0; c < d; ++c) {
-              const int64_t x = kv_index(&P, b, j, hk, c);
-              const double qc = elem(q, in_bf16, q_index(&P, b, i, h, c));
-              const double doc = elem(dout, in_bf16, q_index(&P, b, i, h, c));
-              dk[x] += scale * ds[j] * qc;
-              dv[x] += prob[j] * doc;
-              if (dk_abs) dk_abs[x] += scale * fabs(ds[j]) * fabs(qc);
-              if (dv_abs) dv_abs[x] += prob[j] * fabs(doc);
-            }
-          }
+          dq[q_index(&P, b, i, h, c)] = scale * acc;
+          if (dq_abs) dq_abs[q_index(&P, b, i, h, c)] = scale * acc_abs;
+        }
+      }
+      free(s);
+      free(o_row);
+    }
+    /* step 2: dK_j = scale sum_rows dS_j q,  dV_j = sum_rows P_j dO */
+    #pragma omp parallel for schedule(dynamic, 4)
+    for (int j = 0; j < Sk; ++j) {
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int h = hk * G + (int)(r / Sq), i = (int)(r % Sq);
+        const double *prob = p_all + r * rowlen, *ds = ds_all + r * rowlen;
+        if (prob[j] == 0.0) continue;
+        for (int c = 0; c < d; ++c) {
+          const int64_t x = kv_index(&P, b, j, hk, c);
+          const double qc = elem(q, in_bf16, q_index(&P, b, i, h, c));
+          const double doc = elem(dout, in_bf16, q_index(&P, b, i, h, c));
+          dk[x] += scale * ds[j] * qc;
+          dv[x] += prob[j] * doc;
+          if (dk_abs) dk_abs[x] += scale * fabs(ds[j]) * fabs(qc);
+          if (dv_abs) dv_abs[x] += prob[j] * fabs(doc);
         }
       }
     }
-    free(s);
-    free(prob);
-    free(ds);
-    free(o_row);
   }
+  free(p_all);
+  free(ds_all);
   return 0;
 }

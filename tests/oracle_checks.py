@@ -409,6 +409,22 @@ def check_backward_invariants(orc):
             assert np.all(dq[b, i, h] == 0.0)
 
 
+def check_backward_units(orc):
+    # Computing chosen (batch, kv head) units alone gives their slices exactly, zeros elsewhere.
+    B, Sq, Sk, Hq, Hkv, d = 2, 5, 6, 4, 2, 3
+    q, k, v = _rand(600, B, Sq, Sk, Hq, Hkv, d)
+    do_ = np.random.default_rng(601).standard_normal(q.shape)
+    full = orc.bwd(q, k, v, do_, True, 0.8)
+    part = orc.bwd(q, k, v, do_, True, 0.8, units=[(1, 0)])
+    g = Hq // Hkv
+    dq_f, dk_f, dv_f, ds_f, _ = full
+    dq_p, dk_p, dv_p, ds_p, _ = part
+    assert np.array_equal(dk_p[1, :, 0], dk_f[1, :, 0]) and np.array_equal(dv_p[1, :, 0], dv_f[1, :, 0])
+    assert np.array_equal(dq_p[1, :, 0:g], dq_f[1, :, 0:g]) and np.array_equal(ds_p[1, 0:g], ds_f[1, 0:g])
+    assert not dk_p[0].any() and not dk_p[1, :, 1].any() and not dq_p[0].any()
+    assert not dq_p[1, :, g:].any() and not ds_p[0].any()
+
+
 def check_backward_bf16_widening(orc):
     rng = np.random.default_rng(12)
     shape_q, shape_kv = (1, 5, 2, 4), (1, 7, 1, 4)
@@ -427,7 +443,8 @@ ALL_CHECKS = [
     check_probability_rows, check_shift_invariance, check_key_permutation, check_gqa_grouping,
     check_online_and_split_agree, check_rows_match_full, check_bf16_widening,
     check_decimal_brute_force, check_backward_worked_example, check_backward_exercise_2,
-    check_backward_finite_differences, check_backward_invariants, check_backward_bf16_widening,
+    check_backward_finite_differences, check_backward_invariants, check_backward_units,
+    check_backward_bf16_widening,
 ]
 
 

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "flashfwd.h")
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(\w+)\(", text, re.M)))
+    return sorted(set(re.findall(r"^(?:int|long long|const char\*)\s+(\w+)\(", text, re.M)))
 
 
 def test_header_matches_binding():
@@ -79,6 +79,36 @@ def test_splitkv_and_combine_reject():
     assert lib.attn_splitkv_combine(O, L, Q, K, 1, 1, 8, 96, 4, None) == 3
     assert lib.attn_splitkv_combine(O, L, Q, K, 1, 1, 8, 128, 0, None) == 6
     assert lib.attn_splitkv_combine(O, L, O, K, 1, 1, 8, 128, 4, None) == 9
+
+
+# More fake addresses for the backward's extra buffers (never dereferenced either).
+DO, DQ, DK, DV, WS = 6 << 32, 7 << 32, 8 << 32, 9 << 32, 10 << 32
+
+
+def call_bwd(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS, **kw):
+    a = dict(GOOD, **kw)
+    return ff.load().attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, a["B"], a["Sq"], a["Sk"],
+                              a["Hq"], a["Hkv"], a["d"], a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=None), 1), (dict(ws=None), 1), (dict(dk=None), 1),
+    (dict(Sk=0), 2), (dict(d=96), 3), (dict(Hq=3, Hkv=2), 4),
+    (dict(dout=DO + 8), 5), (dict(ws=WS + 4), 5), (dict(dq=DQ + 2), 5),
+    (dict(scale=0.0), 7), (dict(scale=float("nan")), 7),
+    (dict(dq=Q), 9), (dict(dk=DV), 9), (dict(ws=O), 9), (dict(dv=DO), 9),
+])
+def test_attn_bwd_rejects(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_workspace_size():
+    # D and the base-2 LSE per row, rows padded to a multiple of 64
+    assert ff.attn_bwd_workspace_floats(4, 4096, 16) == 2 * 4 * 16 * 4096
+    assert ff.attn_bwd_workspace_floats(2, 333, 4) == 2 * 2 * 4 * 384
+    assert ff.attn_bwd_workspace_floats(1, 1, 1) == 128
+    with pytest.raises(ff.FlashFwdError):
+        ff.attn_bwd_workspace_floats(0, 10, 1)
 
 
 def test_efficiency_rule_reproduces_printed_example():
