@@ -12,6 +12,10 @@ Functions (all return float64 numpy arrays):
   online(q, k, v, causal, scale, blk)     -> (o, lse)                         per-row online loop
   split(q, k, v, causal, scale, blk, S)   -> (o_part, lse_part, o, lse)       split + combine
   bwd(q, k, v, dout, causal, scale[, units]) -> (dq, dk, dv, dsum, (dq_abs, dk_abs, dv_abs))
+  varlen(q, k, v, cu_q, cu_k, causal, scale) -> (o [total_q,Hq,d], lse [Hq,total_q])
+  kv_gather(k_cache, v_cache, block_table, seqlen, leftpad, b) -> (k, v) of batch b
+  kvcache(q, k_cache, v_cache, block_table, seqlens, leftpad, causal, scale) -> (o, lse)
+  append(k_new, v_new, k_cache, v_cache, block_table, seqlens) -> (k_cache', v_cache')
                                              backward; dsum = D per row [B,Hq,Sq]; *_abs =
                                              sums of absolute terms (for error bounds)
 
@@ -156,6 +160,71 @@ class Oracle:
                                           dv.ctypes.data, dsum.ctypes.data, dq_a.ctypes.data,
                                           dk_a.ctypes.data, dv_a.ctypes.data), "bwd")
         return dq, dk, dv, dsum, (dq_a, dk_a, dv_a)
+
+    # -- variable-length batches and the paged KV cache ("03 forward CUDA kernel" section 8;
+    # "flash attention V2 code walk-through": cu_seqlens as prefix sums, block_table, the
+    # k_offset with leftpad_k).  Each sequence is an independent problem, so these are the
+    # plain definition above applied per sequence to the rows the layout assigns to it.
+
+    def varlen(self, q, k, v, cu_q, cu_k, causal, scale):
+        """q [total_q,Hq,d], k/v [total_k,Hkv,d]; cu_q, cu_k prefix sums [B+1]: sequence b
+        owns rows cu[b] .. cu[b+1]-1.  O [total_q,Hq,d] and LSE [Hq,total_q]."""
+        total_q, Hq, d = q.shape
+        o = np.zeros((total_q, Hq, d))
+        lse = np.zeros((Hq, total_q))
+        for b in range(len(cu_q) - 1):
+            q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+            if q1 == q0:
+                continue
+            if k1 == k0:   # no key at all: O = 0, LSE = -inf
+                lse[:, q0:q1] = -np.inf
+                continue
+            ob, lb = self.fwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], causal, scale)
+            o[q0:q1] = ob[0]
+            lse[:, q0:q1] = lb[0]
+        return o, lse
+
+    @staticmethod
+    def kv_gather(k_cache, v_cache, block_table, seqlen, leftpad, b):
+        """Keys and values of batch b from a paged cache [num_blocks, page, Hkv, d]: logical
+        cache position t lives in physical block block_table[b, t // page], row t % page;
+        the sequence's keys are positions leftpad .. seqlen-1."""
+        page = k_cache.shape[1]
+        pos = np.arange(int(leftpad), int(seqlen))
+        blk = np.asarray(block_table)[b, pos // page]
+        return k_cache[blk, pos % page], v_cache[blk, pos % page]
+
+    def kvcache(self, q, k_cache, v_cache, block_table, seqlens, leftpad, causal, scale):
+        """q [B,Sq,Hq,d] against each batch's cached keys (kv_gather).  O [B,Sq,Hq,d], LSE
+        [B,Hq,Sq]; a batch without keys gets O = 0, LSE = -inf."""
+        B, Sq, Hq, d = q.shape
+        o = np.zeros((B, Sq, Hq, d))
+        lse = np.full((B, Hq, Sq), -np.inf)
+        for b in range(B):
+            lp = 0 if leftpad is None else int(leftpad[b])
+            kb, vb = self.kv_gather(k_cache, v_cache, block_table, seqlens[b], lp, b)
+            if len(kb) == 0:
+                continue
+            ob, lb = self.fwd(q[b:b + 1], kb[None], vb[None], causal, scale)
+            o[b], lse[b] = ob[0], lb[0]
+        return o, lse
+
+    @staticmethod
+    def append(k_new, v_new, k_cache, v_cache, block_table, seqlens):
+        """Copies of the caches with k_new[b, t], v_new[b, t] written at logical position
+        seqlens[b] + t of batch b (positions past the table's capacity are dropped)."""
+        kc, vc = k_cache.copy(), v_cache.copy()
+        page = k_cache.shape[1]
+        cap = np.asarray(block_table).shape[1] * page
+        for b in range(k_new.shape[0]):
+            for t in range(k_new.shape[1]):
+                p = int(seqlens[b]) + t
+                if p >= cap:
+                    continue
+                blk = block_table[b][p // page]
+                kc[blk, p % page] = k_new[b, t]
+                vc[blk, p % page] = v_new[b, t]
+        return kc, vc
 
 
 _default = None

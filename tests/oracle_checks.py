@@ -437,6 +437,96 @@ def check_backward_bf16_widening(orc):
         assert np.array_equal(a, b)
 
 
+# ---------------------------------------------------------------------------
+# Variable-length batches and the paged KV cache
+
+
+def check_varlen_printed_prefix_sums(orc):
+    g = golden("varlen_cu_seqlens.json")
+    cu = g["cu_seqlens"]
+    assert [cu[i + 1] - cu[i] for i in range(len(cu) - 1)] == g["printed_lengths"]
+    rng = np.random.default_rng(21)
+    total = cu[-1]
+    q = rng.standard_normal((total, 2, 3))
+    k = rng.standard_normal((total, 1, 3))
+    v = rng.standard_normal((total, 1, 3))
+    o, lse = orc.varlen(q, k, v, cu, cu, True, 0.6)
+    # sequences 2 and 3 hold one query and one key: O = v, LSE = that score
+    for r in (248, 249):
+        for h in range(2):
+            assert np.allclose(o[r, h], v[r, 0], rtol=0, atol=TIGHT)
+            assert abs(lse[h, r] - 0.6 * np.dot(q[r, h], k[r, 0])) < TIGHT
+    # sequence 1 is the dense problem on rows 0..247
+    o1, l1 = orc.fwd(q[None, :248], k[None, :248], v[None, :248], True, 0.6)
+    assert np.allclose(o[:248], o1[0], rtol=0, atol=TIGHT)
+    assert np.allclose(lse[:, :248], l1[0], rtol=0, atol=TIGHT)
+
+
+def check_varlen_equal_lengths_and_independence(orc):
+    q, k, v = _rand(700, 3, 5, 6, 4, 2, 3)
+    o_b, l_b = orc.fwd(q, k, v, True, 0.8)
+    cu_q, cu_k = [0, 5, 10, 15], [0, 6, 12, 18]
+    o, lse = orc.varlen(q.reshape(15, 4, 3), k.reshape(18, 2, 3), v.reshape(18, 2, 3),
+                        cu_q, cu_k, True, 0.8)
+    assert np.allclose(o.reshape(3, 5, 4, 3), o_b, rtol=0, atol=TIGHT)
+    assert np.allclose(lse.reshape(4, 3, 5).transpose(1, 0, 2), l_b, rtol=0, atol=TIGHT)
+    # Changing sequence 1's keys leaves the other sequences' outputs alone.
+    k2 = k.reshape(18, 2, 3).copy()
+    k2[6:12] += np.random.default_rng(701).standard_normal(k2[6:12].shape)
+    o2, l2 = orc.varlen(q.reshape(15, 4, 3), k2, v.reshape(18, 2, 3), cu_q, cu_k, True, 0.8)
+    keep = np.r_[0:5, 10:15]
+    assert np.array_equal(o2[keep], o[keep]) and np.array_equal(l2[:, keep], lse[:, keep])
+    assert not np.allclose(o2[5:10], o[5:10])
+    # An empty query sequence and a sequence without keys.
+    o3, l3 = orc.varlen(q.reshape(15, 4, 3)[:10], k.reshape(18, 2, 3)[:6], v.reshape(18, 2, 3)[:6],
+                        [0, 5, 5, 10], [0, 6, 6, 6], False, 0.8)
+    assert np.all(o3[5:10] == 0.0) and np.all(l3[:, 5:10] == -np.inf)
+
+
+def check_paged_cache_gather(orc):
+    rng = np.random.default_rng(22)
+    B, Sq, Hq, Hkv, d, page, nblk = 2, 3, 4, 2, 3, 4, 3
+    q = rng.standard_normal((B, Sq, Hq, d))
+    kc = rng.standard_normal((B * nblk, page, Hkv, d))
+    vc = rng.standard_normal((B * nblk, page, Hkv, d))
+    ident = np.arange(B * nblk).reshape(B, nblk)
+    seqlens, leftpad = [10, 7], [0, 2]
+    o, lse = orc.kvcache(q, kc, vc, ident, seqlens, leftpad, True, 0.7)
+    for b in range(B):
+        kb = kc[ident[b]].reshape(nblk * page, Hkv, d)[leftpad[b]:seqlens[b]]
+        vb = vc[ident[b]].reshape(nblk * page, Hkv, d)[leftpad[b]:seqlens[b]]
+        ob, lb = orc.fwd(q[b:b + 1], kb[None], vb[None], True, 0.7)
+        assert np.allclose(o[b], ob[0], rtol=0, atol=TIGHT) and np.allclose(lse[b], lb[0], rtol=0, atol=TIGHT)
+    # Moving the physical blocks (and the table with them) changes nothing.
+    perm = rng.permutation(B * nblk)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    o2, l2 = orc.kvcache(q, kc2, vc2, perm[ident], seqlens, leftpad, True, 0.7)
+    assert np.array_equal(o2, o) and np.array_equal(l2, lse)
+    # A batch whose keys are all padding: O = 0, LSE = -inf.
+    o3, l3 = orc.kvcache(q, kc, vc, ident, [10, 5], [0, 5], True, 0.7)
+    assert np.all(o3[1] == 0.0) and np.all(l3[1] == -np.inf)
+
+
+def check_cache_append(orc):
+    rng = np.random.default_rng(23)
+    B, S_new, Hkv, d, page, nblk = 2, 3, 2, 2, 4, 2
+    kc = rng.standard_normal((B * nblk, page, Hkv, d))
+    vc = rng.standard_normal((B * nblk, page, Hkv, d))
+    table = np.array([[3, 0], [1, 2]])
+    kn = rng.standard_normal((B, S_new, Hkv, d))
+    vn = rng.standard_normal((B, S_new, Hkv, d))
+    seqlens = [2, 6]                       # batch 1 runs past its capacity of 8 after 2 rows
+    kc2, vc2 = orc.append(kn, vn, kc, vc, table, seqlens)
+    k0, v0 = orc.kv_gather(kc2, vc2, table, 5, 0, 0)
+    assert np.array_equal(k0[:2], orc.kv_gather(kc, vc, table, 2, 0, 0)[0]) and np.array_equal(k0[2:], kn[0])
+    assert np.array_equal(v0[2:], vn[0])
+    k1, _ = orc.kv_gather(kc2, vc2, table, 8, 0, 1)
+    assert np.array_equal(k1[6:], kn[1, :2]) and np.array_equal(k1[:6], orc.kv_gather(kc, vc, table, 6, 0, 1)[0])
+    changed = np.argwhere(np.any(kc2 != kc, axis=(2, 3)))
+    assert len(changed) == 5            # 3 rows for batch 0, 2 for batch 1
+
+
 ALL_CHECKS = [
     check_online_softmax_example, check_one_query_two_keys, check_exercise_1, check_exercise_2,
     check_causal_mask_pictures, check_tail_tile_case, check_special_cases,
@@ -444,7 +534,8 @@ ALL_CHECKS = [
     check_online_and_split_agree, check_rows_match_full, check_bf16_widening,
     check_decimal_brute_force, check_backward_worked_example, check_backward_exercise_2,
     check_backward_finite_differences, check_backward_invariants, check_backward_units,
-    check_backward_bf16_widening,
+    check_backward_bf16_widening, check_varlen_printed_prefix_sums,
+    check_varlen_equal_lengths_and_independence, check_paged_cache_gather, check_cache_append,
 ]
 
 
