@@ -158,6 +158,43 @@ def run_prefill(torch, ff, name, steps, warmup):
     return res, (q, k, v)
 
 
+def run_varlen(torch, ff, name, steps, warmup):
+    """attn_fwd_varlen over a packed batch: the flops are those of each sequence on its own."""
+    w = synth.WORKLOADS[name]
+    q, k, v, lens = synth.make_varlen_qkv(w)
+    cu = torch.from_numpy(synth.prefix_sums(lens)).to("cuda:0")
+    qd, kd, vd = (to_dev(torch, x) for x in (q, k, v))
+    del q, k, v
+    T, Hq, Hkv, d = w["total"], w["Hq"], w["Hkv"], w["d"]
+    o = torch.empty((T, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((Hq, T), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ff.attn_fwd_varlen(qd, kd, vd, o, lse, cu, cu, len(lens), max(lens), T, T, Hq, Hkv, d,
+                           w["causal"], w["scale"], stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    t.start()
+    for _ in range(steps):
+        step()
+    ms = t.stop_ms() / steps
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item(), f"{name}: non-finite output"
+    flops = sum(4 * d * visible_pairs(n, n, w["causal"]) * Hq for n in lens)
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {name}: {len(lens)} sequences, {ms:.4f} ms/step, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of dense bf16 peak)")
+    return {"workload": name, "metric": "TFLOP/s", "value": round(tflops, 2),
+            "ms_per_step": round(ms, 4), "kernel": "attn_fwd_prefill",
+            "sequence_lengths": lens, "algorithmic_flop_per_launch": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}}
+
+
 def run_backward(torch, ff, steps, warmup):
     """attn_bwd on causal_prefill's inputs: dO is tensor 3 of the workload's seed, O and LSE
     come from attn_fwd.  A step is the three backward kernels (prep, dK/dV, dQ)."""
@@ -300,6 +337,23 @@ def cpu_baseline(name, inputs, seconds):
                       f"{secs:.1f} s wall"}
 
 
+def describe(name):
+    """The JSON line's config object for workload `name`."""
+    w = synth.WORKLOADS.get(name, synth.WORKLOADS[HEADLINE])
+    kind = "causal" if w["causal"] else "non-causal"
+    if "total" in w:
+        return {"workload": f"{name}: {w['total']} tokens packed in sequences of length "
+                            f"uniform on [1, {w['max_len']}], Hq={w['Hq']} Hkv={w['Hkv']} "
+                            f"d={w['d']} {kind}",
+                "total_tokens": w["total"], "Hq": w["Hq"], "Hkv": w["Hkv"], "d": w["d"],
+                "causal": w["causal"], "parallelism": "none (1 GPU)"}
+    label = name if name in synth.WORKLOADS else f"{name} (on {HEADLINE})"
+    return {"workload": f"{label}: B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} Sq={w['Sq']} "
+                        f"Sk={w['Sk']} d={w['d']} {kind}",
+            "B": w["B"], "Sq": w["Sq"], "Sk": w["Sk"], "Hq": w["Hq"], "Hkv": w["Hkv"],
+            "d": w["d"], "causal": w["causal"], "parallelism": "none (1 GPU)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +397,8 @@ def main():
             results[name] = run_decode(torch, ff, name, args.steps, args.warmup)
         elif name == BACKWARD:
             results[name] = run_backward(torch, ff, args.steps, args.warmup)
+        elif "total" in synth.WORKLOADS[name]:
+            results[name] = run_varlen(torch, ff, name, args.steps, args.warmup)
         else:
             results[name], inputs = run_prefill(torch, ff, name, args.steps, args.warmup)
             if name == HEADLINE:
@@ -356,7 +412,6 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and headline_inputs is not None:
         cpu = cpu_baseline(HEADLINE, headline_inputs, args.cpu_seconds)
-    w = synth.WORKLOADS[main_name if main_name in synth.WORKLOADS else HEADLINE]
     line = {
         "metric": METRIC,
         "value": main["value"],
@@ -370,11 +425,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{main_name}: B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} "
-                               f"Sq={w['Sq']} Sk={w['Sk']} d={w['d']} "
-                               f"{'causal' if w['causal'] else 'non-causal'}",
-                   "B": w["B"], "Sq": w["Sq"], "Sk": w["Sk"], "Hq": w["Hq"], "Hkv": w["Hkv"],
-                   "d": w["d"], "causal": w["causal"], "parallelism": "none (1 GPU)"},
+        "config": describe(main_name),
         "roofline": main["roofline"],
         "cpu_baseline": cpu,
         "workloads": {k: v for k, v in results.items()},

@@ -72,6 +72,25 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
              int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal, float scale,
              void* stream);
 
+/* Forward over a variable-length batch ("03 forward CUDA kernel" section 8: sequences
+ * concatenated without padding, boundaries given by prefix sums; "flash attention V2
+ * code walk-through", Flash_fwd_params: cu_seqlens_q / cu_seqlens_k, q as
+ * (total_q, num_heads, head_size)).  Sequence b owns query rows cu_seqlens_q[b] ..
+ * cu_seqlens_q[b+1]-1 and key/value rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1; each
+ * sequence is attended on its own, causal bottom-right aligned within the sequence.
+ *   q [total_q,Hq,d], k, v [total_k,Hkv,d]: bf16; o [total_q,Hq,d], lse [Hq,total_q]: fp32
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [B+1], non-decreasing, starting at 0 and
+ *     ending at total_q / total_k; max_seqlen_q: the longest query sequence
+ * The prefix sums live on the device and are not checked on the host; the kernel clamps
+ * them to [0, total] so that no access leaves the tensors (a malformed sum yields
+ * unspecified values for the sequences it touches).  A sequence without keys gets O = 0,
+ * LSE = -inf.  Other argument rules and errors as for attn_fwd; the prefix sums need
+ * 4-byte alignment. */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
+                    int total_q, int total_k, int Hq, int Hkv, int d, int causal, float scale,
+                    void* stream);
+
 /* Split count for attn_fwd_splitkv.  The rule is the forward-kernel page's
  * (section 7.2): the smallest split count whose wave efficiency is at least 85%
  * of the best, where efficiency(S) = w / ceil(w) and w = units * S / slots.

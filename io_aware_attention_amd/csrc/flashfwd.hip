@@ -186,6 +186,36 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
   return launch_status();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Fills the work-list fields of p (B, Sq = longest query sequence, Hq, Hkv set) and
+// launches the prefill kernel.
+int launch_prefill(ff::FwdParams& p, int d, int causal, float scale, void* stream) {
+  p.G = p.Hq / p.Hkv;
+  p.num_m = (int)cdiv(p.Sq, ff::PrefillTraits<128>::BM);
+  p.u_per = (int)cdiv((int64_t)p.B * p.Hkv, 8);
+  const int64_t total = 8 * (int64_t)p.u_per * p.G * p.num_m;  // unit slots of all 8 XCDs
+  if (total >= kMaxElems) return FF_ERR_SHAPE;
+  p.total = (int)total;
+  p.scale_log2 = scale * ff::kLog2e;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)total), block(256);
+  if (d == 128) {
+    if (causal) hipLaunchKernelGGL((ff::attn_fwd_prefill<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ff::attn_fwd_prefill<128, false>), grid, block, 0, s, p);
+  } else {
+    if (causal) hipLaunchKernelGGL((ff::attn_fwd_prefill<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ff::attn_fwd_prefill<64, false>), grid, block, 0, s, p);
+  }
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
 int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Sq,
              int Sk, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
   if (!q || !k || !v || !o || !lse) return FF_ERR_NULL;
@@ -198,7 +228,7 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, 
   const int64_t ob[2] = {(int64_t)B * Sq * Hq * d * 4, (int64_t)B * Hq * Sq * 4};
   if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 2))) return st;
 
-  ff::FwdParams p;
+  ff::FwdParams p = {};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
@@ -209,23 +239,52 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, 
   p.Sk = Sk;
   p.Hq = Hq;
   p.Hkv = Hkv;
-  p.G = Hq / Hkv;
-  p.num_m = (int)cdiv(Sq, ff::PrefillTraits<128>::BM);
-  const int64_t total = (int64_t)p.num_m * B * Hq;
-  if (total >= kMaxElems) return FF_ERR_SHAPE;
-  p.total = (int)total;
-  p.u_per = (int)cdiv((int64_t)B * Hkv, 8);
-  p.scale_log2 = scale * ff::kLog2e;
-  hipStream_t s = (hipStream_t)stream;
-  const dim3 grid((unsigned)total), block(256);
-  if (d == 128) {
-    if (causal) hipLaunchKernelGGL((ff::attn_fwd_prefill<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((ff::attn_fwd_prefill<128, false>), grid, block, 0, s, p);
-  } else {
-    if (causal) hipLaunchKernelGGL((ff::attn_fwd_prefill<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((ff::attn_fwd_prefill<64, false>), grid, block, 0, s, p);
-  }
-  return launch_status();
+  p.cu_q = p.cu_k = nullptr;
+  return launch_prefill(p, d, causal, scale, stream);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int max_seqlen_q,
+                    int total_q, int total_k, int Hq, int Hkv, int d, int causal, float scale,
+                    void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FF_ERR_NULL;
+  if (B < 1 || max_seqlen_q < 1 || total_q < 1 || total_k < 1 || Hq < 1 || Hkv < 1)
+    return FF_ERR_SHAPE;
+  if (d != 64 && d != 128) return FF_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FF_ERR_GQA;
+  if ((int64_t)total_q * Hq * d >= kMaxElems || (int64_t)total_k * Hkv * d >= kMaxElems ||
+      max_seqlen_q > total_q)
+    return FF_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+      ((uintptr_t)cu_seqlens_q & 3u) || ((uintptr_t)cu_seqlens_k & 3u))
+    return FF_ERR_ALIGN;
+  int st = check_scale(scale);
+  if (st) return st;
+  // As a [1, total, H, d] problem for the overlap checks.
+  const void* outs[2] = {o, lse};
+  const int64_t ob[2] = {(int64_t)total_q * Hq * d * 4, (int64_t)Hq * total_q * 4};
+  if ((st = check_io(q, k, v, 1, total_q, total_k, Hq, Hkv, d, outs, ob, 2))) return st;
+  for (int i = 0; i < 2; ++i)
+    if (overlaps(outs[i], ob[i], cu_seqlens_q, (int64_t)(B + 1) * 4) ||
+        overlaps(outs[i], ob[i], cu_seqlens_k, (int64_t)(B + 1) * 4))
+      return FF_ERR_ALIAS;
+
+  ff::FwdParams p = {};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Sq = max_seqlen_q;
+  p.Sk = 0;  // per sequence
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  return launch_prefill(p, d, causal, scale, stream);
 }
 
 int attn_splits_efficiency_rule(int units, int slots, int max_splits) {

@@ -45,10 +45,26 @@ struct FwdParams {
   float* lse;
   int B, Sq, Sk, Hq, Hkv, G;  // G = Hq / Hkv
   int num_m;                  // query tiles per (batch, head)
-  int total;                  // num_m * B * Hq workgroups
-  int u_per;                  // (batch, kv head) units per XCD group: ceil(B * Hkv / 8)
+  int total;                  // 8 * u_per * G * num_m workgroups
+  int u_per;                  // (batch, kv head) unit slots per XCD: ceil(B * Hkv / 8)
   float scale_log2;           // scale * log2(e)
+  // Variable-length batches: when cu_q is set, q/o are [total_q, Hq, d], k/v are
+  // [total_k, Hkv, d], sequence b owns rows cu_q[b] .. cu_q[b+1]-1 (keys: cu_k), Sq is
+  // the longest query sequence, and lse is [Hq, total_q].
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
+
+// Rows [start, start + len) of sequence b under prefix sums cu (clamped to [0, total],
+// so that malformed sums cannot send any access out of the tensor).
+__device__ __forceinline__ void seq_range(const int* cu, int b, int total, int* start, int* len) {
+  int a = cu[b], e = cu[b + 1];
+  a = a < 0 ? 0 : (a > total ? total : a);
+  e = e < a ? a : (e > total ? total : e);
+  *start = a;
+  *len = e - a;
+}
 
 // Exponents stay within 2^kRescaleSlack of the stored reference point.
 constexpr float kRescaleSlack = 8.0f;
@@ -114,26 +130,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   constexpr int LOADS = T::LOADS;
   __shared__ __attribute__((aligned(1024))) char smem[T::kLds];
 
-  // ---- which (batch, head, query tile) this workgroup owns.  The work list is cut
-  // into groups of u_per (batch, kv head) units, one group per XCD; inside a group
-  // the order is query tile (heaviest first when causal), then unit, then query
-  // head of the unit, so each XCD starts its longest tiles first.
+  // ---- which (batch, head, query tile) this workgroup owns.  Each XCD gets u_per
+  // (batch, kv head) unit slots: XCD x holds units x, x + 8, x + 16, ... of the
+  // batch-major unit list (slots past the last unit are idle), so that the kv heads of
+  // one sequence spread over the XCDs and sequences of different length load them
+  // evenly.  Inside an XCD the order is query tile (heaviest first when causal), then
+  // unit, then query head of the unit, so each XCD starts its longest tiles first.
   const int idx = xcd_remap(blockIdx.x, p.total);
-  const int U = p.B * p.Hkv;
   const int grp = p.u_per * p.G * p.num_m;
   const int sg = idx / grp;
   const int r0 = idx - sg * grp;
-  const int n_units = (U - sg * p.u_per) < p.u_per ? (U - sg * p.u_per) : p.u_per;
-  const int mi = r0 / (n_units * p.G);
-  const int rest = r0 - mi * n_units * p.G;
-  const int unit = sg * p.u_per + rest / p.G;
+  const int mi = r0 / (p.u_per * p.G);
+  const int rest = r0 - mi * p.u_per * p.G;
+  const int unit = (rest / p.G) * 8 + sg;
+  if (unit >= p.B * p.Hkv) return;
   const int hg = rest % p.G;
   const int hk = unit % p.Hkv;
   const int b = unit / p.Hkv;
   const int h = hk * p.G + hg;
   const int mblk = CAUSAL ? p.num_m - 1 - mi : mi;  // heaviest causal tiles first
   const int q0 = mblk * BM;
-  const int Sq = p.Sq, Sk = p.Sk;
+  // this sequence's rows: q rows q_start .. q_start + Sq - 1, k/v rows k_start ..
+  int q_start, Sq, k_start, Sk;
+  int64_t lse_base;  // LSE index of the sequence's row 0 for this head
+  if (p.cu_q) {
+    seq_range(p.cu_q, b, p.total_q, &q_start, &Sq);
+    seq_range(p.cu_k, b, p.total_k, &k_start, &Sk);
+    lse_base = (int64_t)h * p.total_q + q_start;
+  } else {
+    q_start = b * p.Sq;
+    Sq = p.Sq;
+    k_start = b * p.Sk;
+    Sk = p.Sk;
+    lse_base = ((int64_t)b * p.Hq + h) * Sq;
+  }
+  if (q0 >= Sq) return;  // past the end of a shorter sequence
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -164,10 +195,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
 
   if (n_max <= 0) {  // no visible key for any row of this tile
     if (qrow < Sq) {
-      float* orow = p.o + ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D;
+      float* orow = p.o + ((int64_t)q_start + qrow) * q_stride + (int64_t)h * D;
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       for (int c = H * 4; c < D; c += 8) st16f(orow + c, z);
-      if (H == 0) p.lse[((int64_t)b * p.Hq + h) * Sq + qrow] = -INFINITY;
+      if (H == 0) p.lse[lse_base + qrow] = -INFINITY;
     }
     return;
   }
@@ -175,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   // ---- Q^T fragments (GEMM0 B operand): Q[qrow][16c + 8H .. +7]
   u32x4 qf[D / 16];
   {
-    const uint16_t* qp = p.q + ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D + 8 * H;
+    const uint16_t* qp = p.q + ((int64_t)q_start + qrow) * q_stride + (int64_t)h * D + 8 * H;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
       if (qrow < Sq) qf[c] = ld16(qp + 16 * c);
@@ -189,8 +220,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   // ---- direct HBM -> LDS loads.  Wave w, load k fills the 1 KiB LDS block
   // LOADS*w + k: lane i writes chunk slot 64*(LOADS*w + k) + i, i.e. row slot/CPR,
   // physical chunk slot%CPR, which holds logical chunk (physical ^ key(row)).
-  const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)b * Sk * p.Hkv + hk) * D * 2;
-  const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)b * Sk * p.Hkv + hk) * D * 2;
+  const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)k_start * p.Hkv + hk) * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)k_start * p.Hkv + hk) * D * 2;
   int koff[LOADS], voff[LOADS];
 #pragma unroll
   for (int k = 0; k < LOADS; ++k) {
@@ -442,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (qrow < Sq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* orow = p.o + ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D;
+    float* orow = p.o + ((int64_t)q_start + qrow) * q_stride + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -452,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
         st16f(orow + 32 * db + 8 * j + 4 * H, val);
       }
     if (H == 0)
-      p.lse[((int64_t)b * p.Hq + h) * Sq + qrow] =
+      p.lse[lse_base + qrow] =
           l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
   }
 #endif

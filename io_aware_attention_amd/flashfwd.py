@@ -18,9 +18,9 @@ FF_SPLIT_BLOCK_N = 128
 STATUS_NAMES = {0: "FF_OK", 1: "FF_ERR_NULL", 2: "FF_ERR_SHAPE", 3: "FF_ERR_HEADDIM",
                 4: "FF_ERR_GQA", 5: "FF_ERR_ALIGN", 6: "FF_ERR_SPLITS", 7: "FF_ERR_SCALE",
                 8: "FF_ERR_HIP", 9: "FF_ERR_ALIAS"}
-EXPORTS = ("attn_fwd", "attn_splitkv_num_splits", "attn_splits_efficiency_rule",
-           "attn_fwd_splitkv", "attn_splitkv_combine", "attn_bwd_workspace_floats", "attn_bwd",
-           "attn_status_string")
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_splitkv_num_splits",
+           "attn_splits_efficiency_rule", "attn_fwd_splitkv", "attn_splitkv_combine",
+           "attn_bwd_workspace_floats", "attn_bwd", "attn_status_string")
 
 
 class FlashFwdError(RuntimeError):
@@ -58,6 +58,7 @@ def load(path=LIB_PATH):
     lib = ctypes.CDLL(os.path.abspath(path))
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+    lib.attn_fwd_varlen.argtypes = [P] * 7 + [I] * 8 + [F, P]
     lib.attn_splitkv_num_splits.argtypes = [I, I, I, I, I, I, I]
     lib.attn_splits_efficiency_rule.argtypes = [I, I, I]
     lib.attn_fwd_splitkv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
@@ -105,6 +106,14 @@ def attn_status_string(status):
 def attn_fwd(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream=None):
     _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv,
                            d, int(bool(causal)), float(scale), _stream(stream)), "attn_fwd")
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, total_q,
+                    total_k, Hq, Hkv, d, causal, scale, stream=None):
+    _check(load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, max_seqlen_q,
+                                  total_q, total_k, Hq, Hkv, d, int(bool(causal)), float(scale),
+                                  _stream(stream)), "attn_fwd_varlen")
 
 
 def attn_splitkv_num_splits(B, Sq, Sk, Hq, Hkv, d, num_cus=0):
@@ -160,6 +169,21 @@ def forward(q, k, v, causal, scale, stream=None):
     o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     attn_fwd(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream)
+    return o, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, scale,
+                   stream=None):
+    """O [total_q,Hq,d] fp32 and LSE [Hq,total_q] fp32 from bf16 q [total_q,Hq,d] and k/v
+    [total_k,Hkv,d], with int32 device prefix sums cu_seqlens_q/k [B+1]."""
+    import torch
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    B = cu_seqlens_q.numel() - 1
+    o = torch.empty((total_q, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, total_q,
+                    total_k, Hq, Hkv, d, causal, scale, stream)
     return o, lse
 
 

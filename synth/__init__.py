@@ -94,7 +94,31 @@ WORKLOADS = {
                        scale=f32(1 / np.sqrt(128.0)), seed=4, mult=1.0),
     "long_causal_gqa": dict(B=1, Sq=16384, Sk=16384, Hq=32, Hkv=8, d=128, causal=True,
                             scale=f32(1 / np.sqrt(128.0)), seed=5, mult=0.5),
+    # causal_prefill's 16384 tokens as a packed batch of sequences of mixed length
+    # (seq_lengths: uniform on [1, 4096]); q/k/v [16384, H, d], cu_seqlens prefix sums
+    "varlen_prefill": dict(total=16384, max_len=4096, Hq=16, Hkv=16, d=128, causal=True,
+                           scale=f32(1 / np.sqrt(128.0)), seed=6, mult=1.0),
 }
+
+
+def seq_lengths(seed, tensor_id, total, max_len, min_len=1):
+    """Sequence lengths, each uniform on [min_len, max_len], drawn until they reach total
+    tokens (the last one is cut so that they sum to total exactly)."""
+    u = uniforms(seed, tensor_id, total)
+    out, acc = [], 0
+    for x in u:
+        if acc >= total:
+            break
+        n = min_len + int(x * (max_len - min_len + 1))
+        n = min(n, max_len, total - acc)
+        out.append(n)
+        acc += n
+    return out
+
+
+def prefix_sums(lengths):
+    """[0, l0, l0+l1, ...] as int32."""
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
 
 
 def make_qkv(w):
@@ -103,3 +127,13 @@ def make_qkv(w):
     k = normal_bf16(w["seed"], 1, (w["B"], w["Sk"], w["Hkv"], w["d"]), w["mult"])
     v = normal_bf16(w["seed"], 2, (w["B"], w["Sk"], w["Hkv"], w["d"]), w["mult"])
     return q, k, v
+
+
+def make_varlen_qkv(w):
+    """(q, k, v, lengths) for a packed workload: lengths from seq_lengths (stream 9), q
+    [total,Hq,d], k/v [total,Hkv,d] bf16 bits; keys and queries share the lengths."""
+    lengths = seq_lengths(w["seed"], 9, w["total"], w["max_len"])
+    q = normal_bf16(w["seed"], 0, (w["total"], w["Hq"], w["d"]), w["mult"])
+    k = normal_bf16(w["seed"], 1, (w["total"], w["Hkv"], w["d"]), w["mult"])
+    v = normal_bf16(w["seed"], 2, (w["total"], w["Hkv"], w["d"]), w["mult"])
+    return q, k, v, lengths

@@ -67,6 +67,30 @@ def test_attn_fwd_rejects(kw, code):
     assert call_fwd(**kw) == code
 
 
+CQ, CK = 11 << 32, 12 << 32   # fake prefix-sum arrays
+VGOOD = dict(B=2, max_q=8, total_q=12, total_k=12, Hq=2, Hkv=1, d=64, causal=1, scale=0.125)
+
+
+def call_varlen(q=Q, k=K, v=V, o=O, lse=L, cq=CQ, ck=CK, **kw):
+    a = dict(VGOOD, **kw)
+    return ff.load().attn_fwd_varlen(q, k, v, o, lse, cq, ck, a["B"], a["max_q"], a["total_q"],
+                                     a["total_k"], a["Hq"], a["Hkv"], a["d"], a["causal"],
+                                     a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cq=None), 1), (dict(ck=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(max_q=0), 2), (dict(total_q=0), 2), (dict(total_k=0), 2),
+    (dict(max_q=13), 2), (dict(total_q=1 << 24, Hq=1 << 4, d=128), 2),
+    (dict(d=80), 3), (dict(Hq=3, Hkv=2), 4),
+    (dict(cq=CQ + 2), 5), (dict(k=K + 8), 5),
+    (dict(scale=0.0), 7),
+    (dict(o=K), 9), (dict(lse=CQ), 9), (dict(cq=O + 64), 9),
+])
+def test_attn_fwd_varlen_rejects(kw, code):
+    assert call_varlen(**kw) == code
+
+
 def test_splitkv_and_combine_reject():
     lib = ff.load()
     a = (1, 1, 300, 8, 2, 128, 0, 0.1)
