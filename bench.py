@@ -245,6 +245,21 @@ def run_decode(torch, ff, name, steps, warmup):
     del k, v
     B, Sq, Sk, Hq, Hkv, d = (w[x] for x in ("B", "Sq", "Sk", "Hq", "Hkv", "d"))
     S = ff.attn_splitkv_num_splits(B, Sq, Sk, Hq, Hkv, d)
+    page = w.get("page")
+    if page:
+        # the same keys and values moved into blocks of `page` positions in a random order
+        mb = Sk // page
+        table = np.random.default_rng(w["seed"]).permutation(B * mb).astype(np.int32)
+        tb = torch.from_numpy(table).long().to("cuda:0")
+        kc = torch.empty((B * mb, page, Hkv, d), dtype=torch.bfloat16, device="cuda:0")
+        vc = torch.empty_like(kc)
+        kc[tb] = kd.view(B * mb, page, Hkv, d)
+        vc[tb] = vd.view(B * mb, page, Hkv, d)
+        kd, vd = kc, vc
+        table_d = torch.from_numpy(table.reshape(B, mb)).to("cuda:0")
+        seqlens = torch.full((B,), Sk, dtype=torch.int32, device="cuda:0")
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda:0")
     oa = torch.empty((S, B, Hq, Sq, d), dtype=torch.float32, device="cuda:0")
@@ -256,7 +271,11 @@ def run_decode(torch, ff, name, steps, warmup):
     def step(i=None):
         if i is not None:
             ev[i][0].record(stream)
-        if S == 1:
+        if page:
+            ff.attn_fwd_kvcache(qd, kd, vd, seqlens, None, table_d, oa if S > 1 else None,
+                                la if S > 1 else None, o, lse, B, Sq, Hq, Hkv, d, B * mb, page,
+                                mb, 0, w["causal"], w["scale"], S, stream)
+        elif S == 1:
             ff.attn_fwd_splitkv(qd, kd, vd, None, None, o, lse, B, Sq, Sk, Hq, Hkv, d,
                                 w["causal"], w["scale"], 1, stream)
         else:
@@ -286,6 +305,7 @@ def run_decode(torch, ff, name, steps, warmup):
         "workload": name, "metric": "GB/s", "value": round(step_gbs, 1),
         "ms_per_step": round(ms, 4), "num_splits": S,
         "kernel": "attn_fwd_splitkv", "kernel_ms": round(split_ms, 4),
+        "kv_layout": f"paged, {page}-position blocks" if page else "dense",
         "algorithmic_bytes_per_step": kvb + qb + ob + lb,
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / PEAK_HBM_GBS, 4),
@@ -393,7 +413,7 @@ def main():
     headline_inputs = None
     for name in names:
         log(f"[bench] running {name} ...")
-        if name == DECODE:
+        if name in (DECODE, "paged_decode"):
             results[name] = run_decode(torch, ff, name, args.steps, args.warmup)
         elif name == BACKWARD:
             results[name] = run_backward(torch, ff, args.steps, args.warmup)

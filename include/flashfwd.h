@@ -129,6 +129,51 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v,
 int attn_splitkv_combine(const float* o_accum, const float* lse_accum, float* o, float* lse,
                          int B, int Sq, int Hq, int d, int num_splits, void* stream);
 
+/* Split-KV forward against a key/value cache (the decode path of "03 forward CUDA
+ * kernel" section 8, which sends cached attention through the split-KV kernel; "flash
+ * attention V2 code walk-through": block_table in Flash_fwd_params, the paged row offsets
+ * of the split-KV kernel's data preparation, and k_offset with leftpad_k in BlockInfo).
+ *   q [B,Sq,Hq,d] bf16; outputs as for attn_fwd_splitkv (o [B,Sq,Hq,d], lse [B,Hq,Sq];
+ *     or the partials for attn_splitkv_combine when num_splits > 1).
+ *   Paged (block_table != NULL): k_cache, v_cache [num_blocks, page_size, Hkv, d] bf16;
+ *     block_table [B, max_blocks_per_seq] int32: logical position t of batch b lives in
+ *     block block_table[b][t / page_size], row t % page_size.  page_size must be a
+ *     multiple of 32.
+ *   Contiguous (block_table == NULL): k_cache, v_cache [B, page_size, Hkv, d], page_size
+ *     being the capacity; num_blocks and max_blocks_per_seq are ignored.
+ *   cache_seqlens [B] int32: batch b's keys end at position cache_seqlens[b] + new_keys
+ *     (new_keys >= 0: rows written by attn_kvcache_append just before, or 0).
+ *   cache_leftpad [B] int32 or NULL: batch b's keys start at position cache_leftpad[b]
+ *     (left padding; NULL = 0).
+ * Causal masking is bottom-right aligned: query i sees key position j iff
+ * j <= i + end_b - Sq.  Each split takes an equal share of its batch's keys, so a short
+ * sequence in a long cache does not leave splits idle.  The device arrays are not read
+ * on the host; the kernel clamps lengths to [0, capacity], left padding to [0, length]
+ * and block numbers to [0, num_blocks - 1], so no access leaves the caches (bad values
+ * give unspecified results for their batch).  A batch without keys gets O = 0,
+ * LSE = -inf.  Errors: FF_ERR_SHAPE also for page_size not a multiple of 32 (paged) and
+ * capacities of 2^31 positions or more; int32 arrays need 4-byte alignment.  The caches
+ * are read only. */
+int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                     const int* cache_seqlens, const int* cache_leftpad, const int* block_table,
+                     float* o_accum, float* lse_accum, float* o, float* lse, int B, int Sq,
+                     int Hq, int Hkv, int d, int num_blocks, int page_size,
+                     int max_blocks_per_seq, int new_keys, int causal, float scale,
+                     int num_splits, void* stream);
+
+/* In-place append of new keys and values to a cache ("03 forward CUDA kernel" section 8;
+ * the walk-through's Append_KV case, new k/v given as knew/vnew): k_new[b][t] and
+ * v_new[b][t] ([B, S_new, Hkv, d] bf16) are written at logical position
+ * cache_seqlens[b] + t of batch b, with the cache layout, block table and clamping of
+ * attn_fwd_kvcache; positions at or past the capacity are dropped.  cache_seqlens is not
+ * updated: pass new_keys = S_new to attn_fwd_kvcache on the same stream.  Batches whose
+ * block tables share a block race on it.  Errors as for attn_fwd_kvcache; the new rows
+ * must not overlap the caches. */
+int attn_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int* cache_seqlens, const int* block_table, int B, int S_new,
+                        int Hkv, int d, int num_blocks, int page_size, int max_blocks_per_seq,
+                        void* stream);
+
 /* Size of attn_bwd's workspace, in floats: 2 * B * Hq * roundup(Sq, 64).  Returns the
  * count, or the negated ff_status (FF_ERR_SHAPE) for B, Sq or Hq below 1. */
 long long attn_bwd_workspace_floats(int B, int Sq, int Hq);

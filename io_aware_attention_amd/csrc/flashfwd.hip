@@ -45,6 +45,28 @@ int check_dims(int B, int Sq, int Sk, int Hq, int Hkv, int d) {
   return FF_OK;
 }
 
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// Cache geometry shared by attn_fwd_kvcache and attn_kvcache_append.  With a block table
+// the caches hold num_blocks blocks of page_size positions (page_size a multiple of 32)
+// and a batch addresses max_blocks_per_seq of them; without one they are [B, page_size,
+// ...] and the other two sizes are ignored.  `extra` new keys must fit on top of a full
+// cache in an int.  Returns the block count and a batch's capacity in positions.
+int check_cache(int B, int Hkv, const int* block_table, int num_blocks, int page_size,
+                int max_blocks_per_seq, int extra, int64_t* blocks, int64_t* cap) {
+  if (B < 1 || Hkv < 1 || page_size < 1 || extra < 0) return FF_ERR_SHAPE;
+  if (block_table) {
+    if (num_blocks < 1 || max_blocks_per_seq < 1 || page_size % 32 != 0) return FF_ERR_SHAPE;
+    *blocks = num_blocks;
+    *cap = (int64_t)max_blocks_per_seq * page_size;
+  } else {
+    *blocks = B;
+    *cap = page_size;
+  }
+  if (*cap + extra >= kMaxElems || *blocks * page_size >= kMaxElems) return FF_ERR_SHAPE;
+  return FF_OK;
+}
+
 int check_scale(float scale) {
   if (!isfinite(scale) || !(scale > 0.f)) return FF_ERR_SCALE;
   return FF_OK;
@@ -367,8 +389,133 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o_accum
   if (total >= kMaxElems) return FF_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
-  if (d == 128) hipLaunchKernelGGL(ff::attn_fwd_splitkv<128>, grid, block, 0, s, p);
-  else hipLaunchKernelGGL(ff::attn_fwd_splitkv<64>, grid, block, 0, s, p);
+  if (d == 128) hipLaunchKernelGGL((ff::attn_fwd_splitkv<128, false>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((ff::attn_fwd_splitkv<64, false>), grid, block, 0, s, p);
+  return launch_status();
+}
+
+int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                     const int* cache_seqlens, const int* cache_leftpad, const int* block_table,
+                     float* o_accum, float* lse_accum, float* o, float* lse, int B, int Sq,
+                     int Hq, int Hkv, int d, int num_blocks, int page_size,
+                     int max_blocks_per_seq, int new_keys, int causal, float scale,
+                     int num_splits, void* stream) {
+  if (!q || !k_cache || !v_cache || !cache_seqlens) return FF_ERR_NULL;
+  if (num_splits < 1 || num_splits > FF_MAX_SPLITS) return FF_ERR_SPLITS;
+  if (num_splits == 1 && (!o || !lse)) return FF_ERR_NULL;
+  if (num_splits > 1 && (!o_accum || !lse_accum)) return FF_ERR_NULL;
+  int64_t blocks = 0, cap = 0;
+  int st = check_cache(B, Hkv, block_table, num_blocks, page_size, max_blocks_per_seq, new_keys,
+                       &blocks, &cap);
+  if (st) return st;
+  if (Sq < 1 || Hq < 1) return FF_ERR_SHAPE;
+  if (d != 64 && d != 128) return FF_ERR_HEADDIM;
+  if (Hq % Hkv != 0) return FF_ERR_GQA;
+  const int64_t rows_all = (int64_t)B * Hq * Sq;
+  if (rows_all * d >= kMaxElems || (int64_t)num_splits * rows_all * d >= kMaxElems)
+    return FF_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(cache_seqlens) ||
+      !aligned4(cache_leftpad) || !aligned4(block_table))
+    return FF_ERR_ALIGN;
+  if (num_splits == 1 && (!aligned16(o) || !aligned16(lse))) return FF_ERR_ALIGN;
+  if (num_splits > 1 && (!aligned16(o_accum) || !aligned16(lse_accum))) return FF_ERR_ALIGN;
+  if ((st = check_scale(scale))) return st;
+  const int64_t cache_b = blocks * page_size * Hkv * d * 2;
+  const void* ins[6] = {q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table};
+  const int64_t in_b[6] = {rows_all * d * 2, cache_b, cache_b, (int64_t)B * 4, (int64_t)B * 4,
+                           (int64_t)B * max_blocks_per_seq * 4};
+  const void* outs[2];
+  int64_t ob[2];
+  if (num_splits == 1) {
+    outs[0] = o, outs[1] = lse, ob[0] = rows_all * d * 4, ob[1] = rows_all * 4;
+  } else {
+    outs[0] = o_accum, outs[1] = lse_accum;
+    ob[0] = num_splits * rows_all * d * 4, ob[1] = num_splits * rows_all * 4;
+  }
+  if (overlaps(outs[0], ob[0], outs[1], ob[1])) return FF_ERR_ALIAS;
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], ob[i], ins[j], in_b[j])) return FF_ERR_ALIAS;
+
+  ff::SplitParams p = {};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k_cache;
+  p.v = (const uint16_t*)v_cache;
+  p.o_accum = o_accum;
+  p.lse_accum = lse_accum;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = 0;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.rows = Sq * p.G;
+  p.num_mb = (int)cdiv(p.rows, kSplitRows);
+  p.num_splits = num_splits;
+  p.split_keys = 0;
+  p.causal = (causal && Sq > 1) ? 1 : 0;
+  p.scale_log2 = scale * ff::kLog2e;
+  p.kv_seqlens = cache_seqlens;
+  p.leftpad = cache_leftpad;
+  p.block_table = block_table;
+  p.num_blocks = (int)blocks;
+  p.page = page_size;
+  p.max_blocks = block_table ? max_blocks_per_seq : 1;
+  p.new_keys = new_keys;
+  const int64_t total = (int64_t)B * Hkv * p.num_mb * num_splits;
+  if (total >= kMaxElems) return FF_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)total), block(256);
+  if (d == 128) hipLaunchKernelGGL((ff::attn_fwd_splitkv<128, true>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((ff::attn_fwd_splitkv<64, true>), grid, block, 0, s, p);
+  return launch_status();
+}
+
+int attn_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int* cache_seqlens, const int* block_table, int B, int S_new,
+                        int Hkv, int d, int num_blocks, int page_size, int max_blocks_per_seq,
+                        void* stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !cache_seqlens) return FF_ERR_NULL;
+  int64_t blocks = 0, cap = 0;
+  int st = check_cache(B, Hkv, block_table, num_blocks, page_size, max_blocks_per_seq, S_new,
+                       &blocks, &cap);
+  if (st) return st;
+  if (S_new < 1) return FF_ERR_SHAPE;
+  if (d != 64 && d != 128) return FF_ERR_HEADDIM;
+  const int64_t new_elems = (int64_t)B * S_new * Hkv * d;
+  if (new_elems >= kMaxElems) return FF_ERR_SHAPE;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned4(cache_seqlens) || !aligned4(block_table))
+    return FF_ERR_ALIGN;
+  const int64_t cache_b = blocks * page_size * Hkv * d * 2;
+  const void* ins[4] = {k_new, v_new, cache_seqlens, block_table};
+  const int64_t in_b[4] = {new_elems * 2, new_elems * 2, (int64_t)B * 4,
+                           (int64_t)B * max_blocks_per_seq * 4};
+  if (overlaps(k_cache, cache_b, v_cache, cache_b)) return FF_ERR_ALIAS;
+  for (int j = 0; j < 4; ++j)
+    if (overlaps(k_cache, cache_b, ins[j], in_b[j]) || overlaps(v_cache, cache_b, ins[j], in_b[j]))
+      return FF_ERR_ALIAS;
+
+  ff::AppendParams p;
+  p.k_new = (const uint16_t*)k_new;
+  p.v_new = (const uint16_t*)v_new;
+  p.k_cache = (uint16_t*)k_cache;
+  p.v_cache = (uint16_t*)v_cache;
+  p.seqlens = cache_seqlens;
+  p.block_table = block_table;
+  p.B = B;
+  p.S_new = S_new;
+  p.Hkv = Hkv;
+  p.num_blocks = (int)blocks;
+  p.page = page_size;
+  p.max_blocks = block_table ? max_blocks_per_seq : 1;
+  p.chunks = new_elems / 8;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)cdiv(p.chunks, 256)), block(256);
+  if (d == 128) hipLaunchKernelGGL(ff::attn_kvcache_append<128>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(ff::attn_kvcache_append<64>, grid, block, 0, s, p);
   return launch_status();
 }
 

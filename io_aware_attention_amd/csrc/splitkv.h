@@ -38,6 +38,15 @@ struct SplitParams {
   int split_keys;   // keys per split (a multiple of the split block)
   int causal;
   float scale_log2;
+  // Key/value cache (the CACHE kernel): k and v hold num_blocks blocks of `page` key
+  // positions, [num_blocks, page, Hkv, d].  Logical position t of batch b lives in block
+  // block_table[b * max_blocks + t / page] (block b when block_table is NULL), row
+  // t % page; batch b's keys are positions leftpad[b] .. kv_seqlens[b] + new_keys - 1.
+  // Each split takes an equal share of its batch's keys.  Sk is unused.
+  const int* kv_seqlens;
+  const int* leftpad;
+  const int* block_table;
+  int num_blocks, page, max_blocks, new_keys;
 };
 
 // Wavefront-local LDS handoff: the lanes of one wavefront exchange data through
@@ -61,7 +70,7 @@ struct SplitTraits {
   static constexpr int kLds = kWaves * WV > kCombine ? kWaves * WV : kCombine;
 };
 
-template <int D>
+template <int D, bool CACHE>
 __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist for the device target only
   using T = SplitTraits<D>;
@@ -82,15 +91,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   const int nr = lane & 15;   // row of this lane in the B operand and the outputs
   const int g4 = lane >> 4;   // which 16-lane group
 
-  const int G = p.G, Sq = p.Sq, Sk = p.Sk;
+  const int G = p.G, Sq = p.Sq;
+  int Sk = p.Sk;
+  int lp = 0;  // first key position (cache left padding)
+  if constexpr (CACHE) {
+    // clamped so that no access leaves the cache, whatever the device arrays hold
+    const int cap = p.max_blocks * p.page;
+    int64_t n = (int64_t)p.kv_seqlens[b] + p.new_keys;
+    Sk = n < 0 ? 0 : (n > cap ? cap : (int)n);
+    if (p.leftpad) {
+      const int a = p.leftpad[b];
+      lp = a < 0 ? 0 : (a > Sk ? Sk : a);
+    }
+  }
   const int R = mb * 16 + nr;
   const bool row_ok = R < p.rows;
   const int qi = R / G;
   const int qh = hk * G + R % G;
 
   // key range of this split, clipped by the causal limit of the block's last row
-  int j_lo = s * p.split_keys;
-  int j_hi = j_lo + p.split_keys < Sk ? j_lo + p.split_keys : Sk;
+  int j_lo, j_hi;
+  if constexpr (CACHE) {
+    // equal shares of whole 128-key blocks from the step holding the first key
+    const int base0 = lp & ~(TK - 1);
+    const int per = (Sk - base0 + p.num_splits - 1) / p.num_splits;
+    const int chunk = (per + NW * TK - 1) / (NW * TK) * (NW * TK);
+    j_lo = base0 + s * chunk;
+    j_hi = j_lo + chunk < Sk ? j_lo + chunk : Sk;
+  } else {
+    j_lo = s * p.split_keys;
+    j_hi = j_lo + p.split_keys < Sk ? j_lo + p.split_keys : Sk;
+  }
   const int r_last = (mb * 16 + 16 < p.rows ? mb * 16 + 16 : p.rows) - 1;
   const int i_first = (mb * 16) / G;
   if (p.causal) {
@@ -115,8 +146,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
       else qf[c] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  const uint16_t* kbase = p.k + (int64_t)b * Sk * kv_stride + (int64_t)hk * D;
-  const uint16_t* vbase = p.v + (int64_t)b * Sk * kv_stride + (int64_t)hk * D;
+  // row 0 of this batch (dense) or of the cache (CACHE) for this key/value head
+  const int64_t brow = CACHE ? 0 : (int64_t)b * Sk;
+  const uint16_t* kbase = p.k + brow * kv_stride + (int64_t)hk * D;
+  const uint16_t* vbase = p.v + brow * kv_stride + (int64_t)hk * D;
   char* wv = smem + wave * T::WV;
 
   f32x4 oacc[D / 16];
@@ -131,15 +164,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   // flight while the current step is computed (two register sets, swapped by
   // unrolling the loop twice).
   // Loads go through buffer descriptors that cover rows j0 .. min(j0 + TK, Sk) - 1
-  // of this key/value head, so rows past Sk read as zero without a branch.
+  // of this key/value head, so rows past Sk read as zero without a branch.  A cache
+  // step (32 aligned keys) lies inside one block, since blocks hold a multiple of 32
+  // positions; V rows before the first key read as zero too (an offset of nrec is out
+  // of range), because the product with a zero probability must not meet stale data.
   const int kv_row_bytes = p.Hkv * D * 2;
   auto load_kv = [&](int j0, u32x4 (&kreg)[2][D / 32], u32x4 (&vreg)[VB][4]) {
     const int rows = Sk - j0 < TK ? Sk - j0 : TK;
     const int nrec = rows > 0 ? rows * kv_row_bytes : 0;
+    int64_t row0 = j0;
+    if constexpr (CACHE) {
+      const int pg = j0 / p.page;
+      int blk = p.block_table ? p.block_table[(int64_t)b * p.max_blocks + pg] : b;
+      blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+      row0 = (int64_t)blk * p.page + (j0 - pg * p.page);
+    }
+    const int lo = lp - j0;  // rows below this are left padding
     const auto rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + (int64_t)j0 * kv_stride), (short)0, nrec, 0x00020000);
+        (void*)(kbase + row0 * kv_stride), (short)0, nrec, 0x00020000);
     const auto rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + (int64_t)j0 * kv_stride), (short)0, nrec, 0x00020000);
+        (void*)(vbase + row0 * kv_stride), (short)0, nrec, 0x00020000);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -151,8 +195,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
       const int blk = lane + 64 * bi;
       const int cg = blk % (D / 8), kg = blk / (D / 8);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vreg[bi][r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (4 * kg + r) * kv_row_bytes + 16 * cg, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        int off = (4 * kg + r) * kv_row_bytes + 16 * cg;
+        if (CACHE && 4 * kg + r < lo) off = nrec;
+        vreg[bi][r] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+      }
     }
   };
   auto compute = [&](int j0, const u32x4 (&kreg)[2][D / 32], const u32x4 (&vreg)[VB][4]) {
@@ -164,13 +211,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) sc[kb] = mfma16(kreg[kb][c], qf[c], sc[kb]);
     }
-    if (j0 + TK > nomask_end) {
+    if (j0 + TK > nomask_end || (CACHE && j0 < lp)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = j0 + 8 * g4 + 4 * kb + i;
-          if (key >= Sk || key > row_lim) sc[kb][i] = -INFINITY;
+          if (key >= Sk || key > row_lim || (CACHE && key < lp)) sc[kb][i] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -352,6 +399,47 @@ __global__ __launch_bounds__(256) void attn_splitkv_combine(CombineParams p) {
 #pragma unroll
   for (int c = 0; c < DPL; ++c) orow[c] = acc[c];
   if (lane == 0) p.lse[row] = L;
+}
+
+// Writes new keys and values into a key/value cache laid out as for the CACHE split
+// kernel: row t of batch b goes to logical position cache_seqlens[b] + t ("03 forward
+// CUDA kernel", section 8: new tokens are appended to the cache in place before the
+// attention reads it).  Positions past the cache's capacity are dropped.  One thread per
+// 16-byte chunk of a (batch, new row, kv head) row, K and V both.
+struct AppendParams {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const int* seqlens;
+  const int* block_table;
+  int B, S_new, Hkv, num_blocks, page, max_blocks;
+  int64_t chunks;  // B * S_new * Hkv * D / 8
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_kvcache_append(AppendParams p) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per head row
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.chunks) return;
+  const int c = (int)(i % CPR);
+  int64_t r = i / CPR;
+  const int h = (int)(r % p.Hkv);
+  r /= p.Hkv;
+  const int t = (int)(r % p.S_new);
+  const int b = (int)(r / p.S_new);
+  const int cap = p.max_blocks * p.page;
+  int n0 = p.seqlens[b];
+  n0 = n0 < 0 ? 0 : (n0 > cap ? cap : n0);
+  const int pos = n0 + t;  // cap + S_new fits in an int (host check)
+  if (pos >= cap) return;
+  const int pg = pos / p.page;
+  int blk = p.block_table ? p.block_table[(int64_t)b * p.max_blocks + pg] : b;
+  blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
+  const int64_t dst = (((int64_t)blk * p.page + (pos - pg * p.page)) * p.Hkv + h) * D + 8 * c;
+  const int64_t src = (((int64_t)b * p.S_new + t) * p.Hkv + h) * D + 8 * c;
+  st16(p.k_cache + dst, ld16(p.k_new + src));
+  st16(p.v_cache + dst, ld16(p.v_new + src));
 }
 
 }  // namespace ff

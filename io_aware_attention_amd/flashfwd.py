@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "FF_OK", 1: "FF_ERR_NULL", 2: "FF_ERR_SHAPE", 3: "FF_ERR_HEAD
                 8: "FF_ERR_HIP", 9: "FF_ERR_ALIAS"}
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_splitkv_num_splits",
            "attn_splits_efficiency_rule", "attn_fwd_splitkv", "attn_splitkv_combine",
-           "attn_bwd_workspace_floats", "attn_bwd", "attn_status_string")
+           "attn_fwd_kvcache", "attn_kvcache_append", "attn_bwd_workspace_floats", "attn_bwd",
+           "attn_status_string")
 
 
 class FlashFwdError(RuntimeError):
@@ -63,6 +64,8 @@ def load(path=LIB_PATH):
     lib.attn_splits_efficiency_rule.argtypes = [I, I, I]
     lib.attn_fwd_splitkv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.attn_splitkv_combine.argtypes = [P, P, P, P, I, I, I, I, I, P]
+    lib.attn_fwd_kvcache.argtypes = [P] * 10 + [I] * 10 + [F, I, P]
+    lib.attn_kvcache_append.argtypes = [P] * 6 + [I] * 7 + [P]
     lib.attn_bwd_workspace_floats.argtypes = [I, I, I]
     lib.attn_bwd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, P]
     lib.attn_status_string.argtypes = [I]
@@ -144,6 +147,24 @@ def attn_splitkv_combine(o_accum, lse_accum, o, lse, B, Sq, Hq, d, num_splits, s
            "attn_splitkv_combine")
 
 
+def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, o_accum,
+                     lse_accum, o, lse, B, Sq, Hq, Hkv, d, num_blocks, page_size,
+                     max_blocks_per_seq, new_keys, causal, scale, num_splits, stream=None):
+    _check(load().attn_fwd_kvcache(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(cache_leftpad),
+        _ptr(block_table), _ptr(o_accum), _ptr(lse_accum), _ptr(o), _ptr(lse), B, Sq, Hq, Hkv,
+        d, num_blocks, page_size, max_blocks_per_seq, new_keys, int(bool(causal)),
+        float(scale), int(num_splits), _stream(stream)), "attn_fwd_kvcache")
+
+
+def attn_kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, B, S_new,
+                        Hkv, d, num_blocks, page_size, max_blocks_per_seq, stream=None):
+    _check(load().attn_kvcache_append(
+        _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+        _ptr(block_table), B, S_new, Hkv, d, num_blocks, page_size, max_blocks_per_seq,
+        _stream(stream)), "attn_kvcache_append")
+
+
 def attn_bwd_workspace_floats(B, Sq, Hq):
     r = load().attn_bwd_workspace_floats(B, Sq, Hq)
     if r < 0:
@@ -207,6 +228,51 @@ def forward_splitkv(q, k, v, causal, scale, num_splits=0, stream=None, return_pa
                      num_splits, stream)
     attn_splitkv_combine(oa, la, o, lse, B, Sq, Hq, d, num_splits, stream)
     return (o, lse, oa, la) if return_partials else (o, lse)
+
+
+def _cache_geometry(k_cache, block_table):
+    if block_table is None:   # contiguous [B, capacity, Hkv, d]
+        B, cap, Hkv, d = k_cache.shape
+        return B, cap, 1, cap, Hkv, d
+    num_blocks, page, Hkv, d = k_cache.shape
+    max_blocks = block_table.shape[1]
+    return num_blocks, page, max_blocks, max_blocks * page, Hkv, d
+
+
+def forward_kvcache(q, k_cache, v_cache, cache_seqlens, causal, scale, block_table=None,
+                    cache_leftpad=None, new_keys=0, num_splits=0, stream=None):
+    """O [B,Sq,Hq,d] and LSE [B,Hq,Sq] (fp32) of bf16 q [B,Sq,Hq,d] against a key/value
+    cache: paged [num_blocks, page, Hkv, d] with int32 block_table [B, max_blocks], or
+    contiguous [B, capacity, Hkv, d] without one.  num_splits = 0 takes
+    attn_splitkv_num_splits' choice for the capacity; more than one split goes through
+    attn_splitkv_combine."""
+    import torch
+    B, Sq, Hq, d = q.shape
+    num_blocks, page, max_blocks, cap, Hkv, _ = _cache_geometry(k_cache, block_table)
+    if num_splits == 0:
+        num_splits = attn_splitkv_num_splits(B, Sq, cap, Hq, Hkv, d)
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    args = (B, Sq, Hq, Hkv, d, num_blocks, page, max_blocks, new_keys, causal, scale)
+    if num_splits == 1:
+        attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, None,
+                         None, o, lse, *args, 1, stream)
+        return o, lse
+    oa = torch.empty((num_splits, B, Hq, Sq, d), dtype=torch.float32, device=q.device)
+    la = torch.empty((num_splits, B, Hq, Sq), dtype=torch.float32, device=q.device)
+    attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, oa, la,
+                     None, None, *args, num_splits, stream)
+    attn_splitkv_combine(oa, la, o, lse, B, Sq, Hq, d, num_splits, stream)
+    return o, lse
+
+
+def kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_table=None,
+                   stream=None):
+    """Writes k_new, v_new [B,S_new,Hkv,d] into the caches at cache_seqlens[b] + t."""
+    B, S_new, Hkv, d = k_new.shape
+    num_blocks, page, max_blocks, _, _, _ = _cache_geometry(k_cache, block_table)
+    attn_kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, B, S_new,
+                        Hkv, d, num_blocks, page, max_blocks, stream)
 
 
 def backward(q, k, v, o, lse, dout, causal, scale, stream=None):

@@ -92,6 +92,10 @@ WORKLOADS = {
                           scale=f32(1 / 8.0), seed=3, mult=1.0),
     "gqa_decode": dict(B=8, Sq=1, Sk=32768, Hq=32, Hkv=8, d=128, causal=False,
                        scale=f32(1 / np.sqrt(128.0)), seed=4, mult=1.0),
+    # gqa_decode's keys and values held in a paged cache of 256-position blocks, dealt to
+    # the batches in a seeded random order (block_table)
+    "paged_decode": dict(B=8, Sq=1, Sk=32768, Hq=32, Hkv=8, d=128, causal=False,
+                         scale=f32(1 / np.sqrt(128.0)), seed=4, mult=1.0, page=256),
     "long_causal_gqa": dict(B=1, Sq=16384, Sk=16384, Hq=32, Hkv=8, d=128, causal=True,
                             scale=f32(1 / np.sqrt(128.0)), seed=5, mult=0.5),
     # causal_prefill's 16384 tokens as a packed batch of sequences of mixed length

@@ -91,6 +91,55 @@ def test_attn_fwd_varlen_rejects(kw, code):
     assert call_varlen(**kw) == code
 
 
+SL, LP, BT, VN = 13 << 32, 14 << 32, 15 << 32, 16 << 32   # seqlens, leftpad, table, v_new
+KGOOD = dict(B=2, Sq=1, Hq=8, Hkv=2, d=128, nb=16, page=64, mb=8, new=0, causal=0,
+             scale=0.1, S=1)
+
+
+def call_kvcache(q=Q, kc=K, vc=V, sl=SL, lp=LP, bt=BT, oa=None, la=None, o=O, lse=L, **kw):
+    a = dict(KGOOD, **kw)
+    return ff.load().attn_fwd_kvcache(q, kc, vc, sl, lp, bt, oa, la, o, lse, a["B"], a["Sq"],
+                                      a["Hq"], a["Hkv"], a["d"], a["nb"], a["page"], a["mb"],
+                                      a["new"], a["causal"], a["scale"], a["S"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sl=None), 1), (dict(kc=None), 1), (dict(o=None), 1), (dict(S=2), 1),
+    (dict(S=0), 6), (dict(S=129), 6),
+    (dict(B=0), 2), (dict(Sq=0), 2), (dict(page=0), 2), (dict(page=48), 2), (dict(nb=0), 2),
+    (dict(mb=0), 2), (dict(new=-1), 2), (dict(mb=1 << 26), 2),
+    (dict(d=96), 3), (dict(Hq=6, Hkv=4), 4),
+    (dict(sl=SL + 2), 5), (dict(bt=BT + 1), 5), (dict(kc=K + 8), 5),
+    (dict(scale=-1.0), 7),
+    (dict(o=K), 9), (dict(lse=SL), 9), (dict(o=BT - 64), 9),
+])
+def test_attn_fwd_kvcache_rejects(kw, code):
+    assert call_kvcache(**kw) == code
+
+
+def test_kvcache_contiguous_ignores_block_counts():
+    # without a block table the caches are [B, page_size, Hkv, d]: page_size need not be a
+    # multiple of 32, and num_blocks / max_blocks_per_seq are not looked at (the call
+    # still fails, on the scale, before any HIP call)
+    assert call_kvcache(bt=None, page=48, nb=0, mb=0, scale=0.0) == 7
+
+
+def call_append(kn=Q, vn=VN, kc=K, vc=V, sl=SL, bt=BT, **kw):
+    a = dict(KGOOD, **kw)
+    return ff.load().attn_kvcache_append(kn, vn, kc, vc, sl, bt, a["B"], a.get("S_new", 4),
+                                         a["Hkv"], a["d"], a["nb"], a["page"], a["mb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), 1), (dict(vc=None), 1), (dict(sl=None), 1),
+    (dict(S_new=0), 2), (dict(page=40), 2), (dict(B=0), 2),
+    (dict(d=32), 3), (dict(vn=VN + 4), 5), (dict(sl=SL + 1), 5),
+    (dict(vc=K), 9), (dict(kn=K + 64), 9), (dict(bt=V + 128), 9),
+])
+def test_attn_kvcache_append_rejects(kw, code):
+    assert call_append(**kw) == code
+
+
 def test_splitkv_and_combine_reject():
     lib = ff.load()
     a = (1, 1, 300, 8, 2, 128, 0, 0.1)
