@@ -21,6 +21,12 @@ Functions (all return float64 numpy arrays):
 
 Inputs are either float64 arrays or uint16 arrays holding bf16 bit patterns (widened
 exactly).  q is [B,Sq,Hq,d]; k and v are [B,Sk,Hkv,d].
+
+fwd, rows, probs, online, split, varlen and kvcache also take the mask and bias variants
+as keywords (the walk-through's Is_local, Has_alibi and Is_softcap):
+  window=(left, right)   sliding window around diag = i + Sk - Sq; -1 = no limit
+  alibi=slopes           [Hq] or [B, Hq]; -slope * |diag - j| is added to the score
+  softcap=c              the scaled score s becomes c * tanh(s / c); 0 = none
 """
 import ctypes
 import os
@@ -47,6 +53,9 @@ _I = ctypes.c_int
 _P = ctypes.c_void_p
 _D = ctypes.c_double
 _COMMON = [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D]
+_OPTS = [_I, _I, _P, _D]   # window_left, window_right, alibi [B, Hq], softcap
+_FWD_FUNCS = ("oracle_attn_fwd", "oracle_attn_rows", "oracle_attn_probs",
+              "oracle_attn_online", "oracle_attn_split")
 
 
 class Oracle:
@@ -60,10 +69,35 @@ class Oracle:
         lib.oracle_attn_online.argtypes = _COMMON + [_I, _P, _P]
         lib.oracle_attn_split.argtypes = _COMMON + [_I, _I, _P, _P, _P, _P]
         lib.oracle_attn_bwd.argtypes = _COMMON + [_P, _P, _P, _P, _P, _P, _P, _P, _P]
-        for f in ("oracle_attn_fwd", "oracle_attn_rows", "oracle_attn_probs",
-                  "oracle_attn_online", "oracle_attn_split", "oracle_attn_bwd"):
+        for f in _FWD_FUNCS:
+            ext = getattr(lib, f + "_ext")
+            ext.argtypes = _COMMON + _OPTS + getattr(lib, f).argtypes[len(_COMMON):]
+            ext.restype = ctypes.c_int
+        for f in _FWD_FUNCS + ("oracle_attn_bwd",):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
+
+    @staticmethod
+    def _opts(B, Hq, window, alibi, softcap):
+        """None for the plain problem, else (ctypes args, keep-alive array)."""
+        wl, wr = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+        if wl == -1 and wr == -1 and alibi is None and not softcap:
+            return None
+        slopes = None
+        if alibi is not None:
+            a = np.asarray(alibi, dtype=np.float64)
+            slopes = np.ascontiguousarray(np.broadcast_to(a if a.ndim == 2 else a[None], (B, Hq)))
+        return ([wl, wr, None if slopes is None else slopes.ctypes.data, float(softcap)], slopes)
+
+    def _call(self, name, a, dims, opts, rest):
+        """Calls name (plain) or name_ext (with the mask/bias options)."""
+        B, Hq = dims[0], dims[3]
+        o = self._opts(B, Hq, *opts)
+        if o is None:
+            rc = getattr(self.lib, name)(*a, *rest)
+        else:
+            rc = getattr(self.lib, name + "_ext")(*a, *o[0], *rest)
+        self._ok(rc, name)
 
     @staticmethod
     def _prep(q, k, v):
@@ -96,45 +130,53 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"{name} returned {rc}")
 
-    def fwd(self, q, k, v, causal, scale):
-        arrs, (B, Sq, Sk, Hq, Hkv, d), a = self._args(q, k, v, causal, scale)
+    def fwd(self, q, k, v, causal, scale, window=None, alibi=None, softcap=0.0):
+        arrs, dims, a = self._args(q, k, v, causal, scale)
+        B, Sq, Sk, Hq, Hkv, d = dims
         o = np.zeros((B, Sq, Hq, d))
         lse = np.zeros((B, Hq, Sq))
-        self._ok(self.lib.oracle_attn_fwd(*a, o.ctypes.data, lse.ctypes.data), "fwd")
+        self._call("oracle_attn_fwd", a, dims, (window, alibi, softcap),
+                   [o.ctypes.data, lse.ctypes.data])
         return o, lse
 
-    def rows(self, q, k, v, causal, scale, rows):
-        arrs, (B, Sq, Sk, Hq, Hkv, d), a = self._args(q, k, v, causal, scale)
+    def rows(self, q, k, v, causal, scale, rows, window=None, alibi=None, softcap=0.0):
+        arrs, dims, a = self._args(q, k, v, causal, scale)
+        d = dims[5]
         r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
         o = np.zeros((len(r), d))
         lse = np.zeros(len(r))
-        self._ok(self.lib.oracle_attn_rows(*a, len(r), r.ctypes.data, o.ctypes.data,
-                                           lse.ctypes.data), "rows")
+        self._call("oracle_attn_rows", a, dims, (window, alibi, softcap),
+                   [len(r), r.ctypes.data, o.ctypes.data, lse.ctypes.data])
         return o, lse
 
-    def probs(self, q, k, v, causal, scale, b, h, i):
-        arrs, (B, Sq, Sk, Hq, Hkv, d), a = self._args(q, k, v, causal, scale)
-        p = np.zeros(Sk)
-        self._ok(self.lib.oracle_attn_probs(*a, b, h, i, p.ctypes.data), "probs")
+    def probs(self, q, k, v, causal, scale, b, h, i, window=None, alibi=None, softcap=0.0):
+        arrs, dims, a = self._args(q, k, v, causal, scale)
+        p = np.zeros(dims[2])
+        self._call("oracle_attn_probs", a, dims, (window, alibi, softcap),
+                   [b, h, i, p.ctypes.data])
         return p
 
-    def online(self, q, k, v, causal, scale, blk):
-        arrs, (B, Sq, Sk, Hq, Hkv, d), a = self._args(q, k, v, causal, scale)
+    def online(self, q, k, v, causal, scale, blk, window=None, alibi=None, softcap=0.0):
+        arrs, dims, a = self._args(q, k, v, causal, scale)
+        B, Sq, Sk, Hq, Hkv, d = dims
         o = np.zeros((B, Sq, Hq, d))
         lse = np.zeros((B, Hq, Sq))
-        self._ok(self.lib.oracle_attn_online(*a, int(blk), o.ctypes.data, lse.ctypes.data),
-                 "online")
+        self._call("oracle_attn_online", a, dims, (window, alibi, softcap),
+                   [int(blk), o.ctypes.data, lse.ctypes.data])
         return o, lse
 
-    def split(self, q, k, v, causal, scale, blk, num_splits):
-        arrs, (B, Sq, Sk, Hq, Hkv, d), a = self._args(q, k, v, causal, scale)
+    def split(self, q, k, v, causal, scale, blk, num_splits, window=None, alibi=None,
+              softcap=0.0):
+        arrs, dims, a = self._args(q, k, v, causal, scale)
+        B, Sq, Sk, Hq, Hkv, d = dims
         S = int(num_splits)
         op = np.zeros((S, B, Hq, Sq, d))
         lp = np.zeros((S, B, Hq, Sq))
         o = np.zeros((B, Sq, Hq, d))
         lse = np.zeros((B, Hq, Sq))
-        self._ok(self.lib.oracle_attn_split(*a, int(blk), S, op.ctypes.data, lp.ctypes.data,
-                                            o.ctypes.data, lse.ctypes.data), "split")
+        self._call("oracle_attn_split", a, dims, (window, alibi, softcap),
+                   [int(blk), S, op.ctypes.data, lp.ctypes.data, o.ctypes.data,
+                    lse.ctypes.data])
         return op, lp, o, lse
 
     def bwd(self, q, k, v, dout, causal, scale, units=None):
@@ -166,7 +208,7 @@ class Oracle:
     # k_offset with leftpad_k).  Each sequence is an independent problem, so these are the
     # plain definition above applied per sequence to the rows the layout assigns to it.
 
-    def varlen(self, q, k, v, cu_q, cu_k, causal, scale):
+    def varlen(self, q, k, v, cu_q, cu_k, causal, scale, **opts):
         """q [total_q,Hq,d], k/v [total_k,Hkv,d]; cu_q, cu_k prefix sums [B+1]: sequence b
         owns rows cu[b] .. cu[b+1]-1.  O [total_q,Hq,d] and LSE [Hq,total_q]."""
         total_q, Hq, d = q.shape
@@ -179,7 +221,8 @@ class Oracle:
             if k1 == k0:   # no key at all: O = 0, LSE = -inf
                 lse[:, q0:q1] = -np.inf
                 continue
-            ob, lb = self.fwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], causal, scale)
+            ob, lb = self.fwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], causal, scale,
+                              **self._batch_opts(opts, b))
             o[q0:q1] = ob[0]
             lse[:, q0:q1] = lb[0]
         return o, lse
@@ -194,7 +237,16 @@ class Oracle:
         blk = np.asarray(block_table)[b, pos // page]
         return k_cache[blk, pos % page], v_cache[blk, pos % page]
 
-    def kvcache(self, q, k_cache, v_cache, block_table, seqlens, leftpad, causal, scale):
+    @staticmethod
+    def _batch_opts(opts, b):
+        """The options of batch b alone (ALiBi slopes [B, Hq] -> [Hq])."""
+        al = opts.get("alibi")
+        if al is not None and np.asarray(al).ndim == 2:
+            opts = dict(opts, alibi=np.asarray(al)[b])
+        return opts
+
+    def kvcache(self, q, k_cache, v_cache, block_table, seqlens, leftpad, causal, scale,
+                **opts):
         """q [B,Sq,Hq,d] against each batch's cached keys (kv_gather).  O [B,Sq,Hq,d], LSE
         [B,Hq,Sq]; a batch without keys gets O = 0, LSE = -inf."""
         B, Sq, Hq, d = q.shape
@@ -205,7 +257,8 @@ class Oracle:
             kb, vb = self.kv_gather(k_cache, v_cache, block_table, seqlens[b], lp, b)
             if len(kb) == 0:
                 continue
-            ob, lb = self.fwd(q[b:b + 1], kb[None], vb[None], causal, scale)
+            ob, lb = self.fwd(q[b:b + 1], kb[None], vb[None], causal, scale,
+                              **self._batch_opts(opts, b))
             o[b], lse[b] = ob[0], lb[0]
         return o, lse
 

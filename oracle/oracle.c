@@ -37,6 +37,19 @@
  *    each range yields (O_s, LSE_s) or (0, -inf) when empty; the combine takes
  *    LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s
  *    (forward-kernel page section 7.3).
+ *  - Mask and bias variants (walk-through, the split-KV kernel's template flags
+ *    Is_local, Has_alibi and Is_softcap, and its n_block_min / n_block_max
+ *    clipping).  With diag = i + Sk - Sq, the key aligned with query i:
+ *      sliding window: key j is visible iff diag - window_left <= j <= diag +
+ *        window_right; a negative bound means no limit on that side.  Causal
+ *        keeps its own limit j <= diag, so causal with a window is the window
+ *        with its right side at most 0 (the pages treat the two as exclusive;
+ *        this is the reading that agrees with both);
+ *      ALiBi: -slope_{b,h} * |diag - j| is added to the score of key j;
+ *      soft cap: the scaled score s becomes c * tanh(s / c) (c > 0; a tanh
+ *        limit on the logits, the page names no formula; this is its plain form).
+ *    The order is: scale, soft cap, ALiBi bias, then the mask.  The soft cap acts
+ *    on the dot-product logit alone and the bias is added to the capped logit.
  *  - Backward (explainer, sections "backward: from the softmax derivative",
  *    "training: backward recomputation" and "backward: back to Q, K, V"): with the
  *    dense probability row P of the plain definition and the upstream gradient dO,
@@ -58,6 +71,9 @@ typedef struct {
   const void *q, *k, *v;
   int B, Sq, Sk, Hq, Hkv, d, causal;
   double scale;
+  int window_left, window_right; /* -1: no limit on that side */
+  const double *alibi;           /* slopes [B, Hq], or NULL */
+  double softcap;                /* 0: none */
 } problem;
 
 static double elem(const void *base, int in_bf16, int64_t idx) {
@@ -74,6 +90,8 @@ static int check(const problem *p) {
   if (!p->q || !p->k || !p->v) return 1;
   if (p->B < 0 || p->Sq < 0 || p->Sk < 0 || p->Hq < 1 || p->Hkv < 1 || p->d < 1) return 2;
   if (p->Hq % p->Hkv != 0) return 3;
+  if (p->window_left < -1 || p->window_right < -1) return 7;
+  if (!(p->softcap >= 0.0) || isinf(p->softcap)) return 8;
   return 0;
 }
 
@@ -87,20 +105,31 @@ static int64_t kv_index(const problem *p, int b, int j, int hk, int c) {
 
 static int kv_head(const problem *p, int h) { return h / (p->Hq / p->Hkv); }
 
-/* Visibility of key j to query i under the bottom-right causal convention. */
+/* Visibility of key j to query i: the bottom-right causal limit and the sliding window,
+ * both measured from diag = i + Sk - Sq. */
 static int visible(const problem *p, int i, int j) {
-  if (!p->causal) return 1;
-  return j <= i + p->Sk - p->Sq;
+  const long long diag = (long long)i + p->Sk - p->Sq;
+  if (p->causal && !(j <= diag)) return 0;
+  if (p->window_left >= 0 && j < diag - p->window_left) return 0;
+  if (p->window_right >= 0 && j > diag + p->window_right) return 0;
+  return 1;
 }
 
-/* Scaled score of query (b,i,h) against key j. */
+/* Logit of query (b,i,h) against key j: the scaled dot product, soft-capped when a cap
+ * is set, plus the ALiBi bias when slopes are given. */
 static double score(const problem *p, int b, int h, int i, int j) {
   int hk = kv_head(p, h);
   double acc = 0.0;
   for (int c = 0; c < p->d; ++c)
     acc += elem(p->q, p->in_bf16, q_index(p, b, i, h, c)) *
            elem(p->k, p->in_bf16, kv_index(p, b, j, hk, c));
-  return p->scale * acc;
+  double s = p->scale * acc;
+  if (p->softcap > 0.0) s = p->softcap * tanh(s / p->softcap);
+  if (p->alibi) {
+    const double dist = (double)((long long)i + p->Sk - p->Sq - j);
+    s -= p->alibi[(int64_t)b * p->Hq + h] * fabs(dist);
+  }
+  return s;
 }
 
 /* Full score row S[0..Sk) with the mask applied, and its probability row P.
@@ -200,16 +229,18 @@ static void online_row(const problem *p, int b, int h, int i, int blk, int t_lo,
   *lse = m + log(l);
 }
 
-#define SETUP_PROBLEM                                                                    \
-  problem P = {in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale};                \
+#define SETUP_PROBLEM_OPTS(WL, WR, ALIBI, CAP)                                          \
+  problem P = {in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale, WL, WR, ALIBI, CAP}; \
   int err = check(&P);                                                                   \
   if (err) return err;
+#define SETUP_PROBLEM SETUP_PROBLEM_OPTS(-1, -1, NULL, 0.0)
 
 /* Plain definition over all rows. o [B,Sq,Hq,d], lse [B,Hq,Sq]. */
-int oracle_attn_fwd(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
-                    int Sk, int Hq, int Hkv, int d, int causal, double scale, double *o,
-                    double *lse) {
-  SETUP_PROBLEM
+int oracle_attn_fwd_ext(int in_bf16, const void *q, const void *k, const void *v, int B,
+                        int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                        int window_left, int window_right, const double *alibi,
+                        double softcap, double *o, double *lse) {
+  SETUP_PROBLEM_OPTS(window_left, window_right, alibi, softcap)
   int64_t nrows = (int64_t)B * Hq * Sq;
   #pragma omp parallel
   {
@@ -229,12 +260,21 @@ int oracle_attn_fwd(int in_bf16, const void *q, const void *k, const void *v, in
   return 0;
 }
 
+int oracle_attn_fwd(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
+                    int Sk, int Hq, int Hkv, int d, int causal, double scale, double *o,
+                    double *lse) {
+  return oracle_attn_fwd_ext(in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale, -1, -1,
+                             NULL, 0.0, o, lse);
+}
+
 /* Plain definition on selected rows.  rows holds nrows triples (b, h, i);
  * o_rows [nrows, d], lse_rows [nrows]. */
-int oracle_attn_rows(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
-                     int Sk, int Hq, int Hkv, int d, int causal, double scale, int nrows,
-                     const int *rows, double *o_rows, double *lse_rows) {
-  SETUP_PROBLEM
+int oracle_attn_rows_ext(int in_bf16, const void *q, const void *k, const void *v, int B,
+                         int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                         int window_left, int window_right, const double *alibi,
+                         double softcap, int nrows, const int *rows, double *o_rows,
+                         double *lse_rows) {
+  SETUP_PROBLEM_OPTS(window_left, window_right, alibi, softcap)
   for (int r = 0; r < nrows; ++r) {
     int b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
     if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= Sq) return 4;
@@ -253,11 +293,19 @@ int oracle_attn_rows(int in_bf16, const void *q, const void *k, const void *v, i
   return 0;
 }
 
+int oracle_attn_rows(int in_bf16, const void *q, const void *k, const void *v, int B,
+                     int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                     int nrows, const int *rows, double *o_rows, double *lse_rows) {
+  return oracle_attn_rows_ext(in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale, -1,
+                              -1, NULL, 0.0, nrows, rows, o_rows, lse_rows);
+}
+
 /* The probability row P[b,h,i,:] of the plain definition (zeros if no key is visible). */
-int oracle_attn_probs(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
-                      int Sk, int Hq, int Hkv, int d, int causal, double scale, int b, int h,
-                      int i, double *prob) {
-  SETUP_PROBLEM
+int oracle_attn_probs_ext(int in_bf16, const void *q, const void *k, const void *v, int B,
+                          int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                          int window_left, int window_right, const double *alibi,
+                          double softcap, int b, int h, int i, double *prob) {
+  SETUP_PROBLEM_OPTS(window_left, window_right, alibi, softcap)
   if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= Sq) return 4;
   double *s = (double *)malloc(sizeof(double) * (Sk > 0 ? Sk : 1));
   double m, l;
@@ -266,11 +314,19 @@ int oracle_attn_probs(int in_bf16, const void *q, const void *k, const void *v, 
   return 0;
 }
 
+int oracle_attn_probs(int in_bf16, const void *q, const void *k, const void *v, int B,
+                      int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                      int b, int h, int i, double *prob) {
+  return oracle_attn_probs_ext(in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale, -1,
+                               -1, NULL, 0.0, b, h, i, prob);
+}
+
 /* Online (tiled) variant with key tile size blk. */
-int oracle_attn_online(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
-                       int Sk, int Hq, int Hkv, int d, int causal, double scale, int blk,
-                       double *o, double *lse) {
-  SETUP_PROBLEM
+int oracle_attn_online_ext(int in_bf16, const void *q, const void *k, const void *v, int B,
+                           int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                           int window_left, int window_right, const double *alibi,
+                           double softcap, int blk, double *o, double *lse) {
+  SETUP_PROBLEM_OPTS(window_left, window_right, alibi, softcap)
   if (blk < 1) return 5;
   int ntiles = (Sk + blk - 1) / blk;
   int64_t nrows = (int64_t)B * Hq * Sq;
@@ -290,15 +346,23 @@ int oracle_attn_online(int in_bf16, const void *q, const void *k, const void *v,
   return 0;
 }
 
+int oracle_attn_online(int in_bf16, const void *q, const void *k, const void *v, int B,
+                       int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                       int blk, double *o, double *lse) {
+  return oracle_attn_online_ext(in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale, -1,
+                                -1, NULL, 0.0, blk, o, lse);
+}
+
 /* Split-KV variant: num_splits contiguous tile ranges, each run with the online
  * loop, then the LSE-weighted combine.  o_part [S,B,Hq,Sq,d] and lse_part
  * [S,B,Hq,Sq] receive the per-split results (either may be NULL); o, lse the
  * combined result. */
-int oracle_attn_split(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
-                      int Sk, int Hq, int Hkv, int d, int causal, double scale, int blk,
-                      int num_splits, double *o_part, double *lse_part, double *o,
-                      double *lse) {
-  SETUP_PROBLEM
+int oracle_attn_split_ext(int in_bf16, const void *q, const void *k, const void *v, int B,
+                          int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                          int window_left, int window_right, const double *alibi,
+                          double softcap, int blk, int num_splits, double *o_part,
+                          double *lse_part, double *o, double *lse) {
+  SETUP_PROBLEM_OPTS(window_left, window_right, alibi, softcap)
   if (blk < 1) return 5;
   if (num_splits < 1) return 6;
   int ntiles = (Sk + blk - 1) / blk;
@@ -351,6 +415,14 @@ int oracle_attn_split(int in_bf16, const void *q, const void *k, const void *v, 
     free(ls);
   }
   return 0;
+}
+
+int oracle_attn_split(int in_bf16, const void *q, const void *k, const void *v, int B,
+                      int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                      int blk, int num_splits, double *o_part, double *lse_part, double *o,
+                      double *lse) {
+  return oracle_attn_split_ext(in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale, -1,
+                               -1, NULL, 0.0, blk, num_splits, o_part, lse_part, o, lse);
 }
 
 /* Backward of the plain definition (see the header).  dout has q's layout and dtype

@@ -527,6 +527,249 @@ def check_cache_append(orc):
     assert len(changed) == 5            # 3 rows for batch 0, 2 for batch 1
 
 
+# ---------------------------------------------------------------------------
+# Mask and bias variants: sliding window, ALiBi, soft cap
+
+
+def _frac(x):
+    a, b = x.split("/")
+    return float(a) / float(b)
+
+
+def _same(r1, r2, tol=TIGHT):
+    (o1, l1), (o2, l2) = r1, r2
+    assert np.allclose(o1, o2, rtol=0, atol=tol), np.abs(o1 - o2).max()
+    assert np.array_equal(np.isneginf(l1), np.isneginf(l2))
+    fin = np.isfinite(l1)
+    assert np.allclose(l1[fin], l2[fin], rtol=0, atol=tol)
+
+
+def check_window_reductions(orc):
+    # Zero ALiBi slopes take the options path and change nothing; the window (-1, 0) is
+    # the causal mask; limits past both ends of the sequence do nothing.
+    for seed, (B, Sq, Sk, Hq, Hkv, d) in enumerate(((2, 5, 9, 4, 2, 3), (1, 9, 4, 2, 2, 3))):
+        q, k, v = _rand(800 + seed, B, Sq, Sk, Hq, Hkv, d)
+        plain = orc.fwd(q, k, v, False, 0.6)
+        causal = orc.fwd(q, k, v, True, 0.6)
+        zeros = np.zeros(Hq)
+        _same(orc.fwd(q, k, v, False, 0.6, alibi=zeros), plain)
+        _same(orc.fwd(q, k, v, True, 0.6, alibi=zeros), causal)
+        _same(orc.fwd(q, k, v, False, 0.6, window=(-1, 0)), causal)
+        _same(orc.fwd(q, k, v, False, 0.6, window=(Sq + Sk, Sq + Sk)), plain)
+        _same(orc.fwd(q, k, v, True, 0.6, window=(Sq + Sk, -1)), causal)
+        _same(orc.fwd(q, k, v, True, 0.6, window=(-1, 3)), causal)
+
+
+def check_window_printed_range(orc):
+    # q = 0 gives uniform weights over the visible keys, and v_j = j then reads off the
+    # visible range: O = (lo + hi) / 2 and LSE = ln(hi - lo + 1) with lo, hi from the
+    # printed range (clipped to the sequence; causal also caps hi at diag).
+    g = golden("mask_variants.json")["window_range"]
+    assert g["no_limit"] == -1
+    for Sq, Sk, wl, wr, causal in ((6, 6, 2, 1, False), (4, 9, 0, 0, False), (9, 4, 1, 2, False),
+                                   (5, 8, 3, -1, False), (5, 8, -1, 2, False), (7, 7, 2, 3, True),
+                                   (3, 10, 4, -1, True), (10, 3, 0, 1, False), (5, 5, 0, 0, True),
+                                   (8, 3, 1, 0, False)):
+        q = np.zeros((1, Sq, 1, 1))
+        k = np.zeros((1, Sk, 1, 1))
+        v = np.arange(Sk, dtype=np.float64).reshape(1, Sk, 1, 1)
+        o, lse = orc.fwd(q, k, v, causal, 1.0, window=(wl, wr))
+        for i in range(Sq):
+            diag = i + Sk - Sq
+            lo = 0 if wl < 0 else max(0, diag - wl)
+            hi = Sk - 1 if wr < 0 else min(Sk - 1, diag + wr)
+            if causal:
+                hi = min(hi, diag)
+            if lo > hi:
+                assert o[0, i, 0, 0] == 0.0 and lse[0, 0, i] == -np.inf, (Sq, Sk, wl, wr, i)
+            else:
+                assert abs(o[0, i, 0, 0] - 0.5 * (lo + hi)) < TIGHT, (Sq, Sk, wl, wr, i)
+                assert abs(lse[0, 0, i] - math.log(hi - lo + 1)) < TIGHT
+
+
+def check_alibi_derived_examples(orc):
+    g = golden("mask_variants.json")["derived"]
+    ln2 = math.log(2.0)
+    e1 = g["alibi_one_sided"]
+    q = np.zeros((1, 1, 1, 1))
+    k = np.zeros((1, 3, 1, 1))
+    v = np.array(e1["v"]).reshape(1, 3, 1, 1)
+    p = orc.probs(q, k, v, False, 1.0, 0, 0, 0, alibi=[ln2])
+    assert np.allclose(p, [_frac(x) for x in e1["P"]], rtol=0, atol=TIGHT), p
+    o, lse = orc.fwd(q, k, v, False, 1.0, alibi=[ln2])
+    assert abs(o[0, 0, 0, 0] - e1["O"]) < TIGHT and abs(lse[0, 0, 0] - math.log(7 / 4)) < TIGHT
+    e2 = g["alibi_two_sided"]
+    q = np.zeros((1, 3, 1, 1))
+    for i, want in e2["rows"].items():
+        p = orc.probs(q, k, v, False, 1.0, 0, 0, int(i), alibi=[ln2])
+        assert np.allclose(p, [_frac(x) for x in want], rtol=0, atol=TIGHT), (i, p)
+    # Slopes [B, Hq]: each (batch, head) uses its own slope.
+    q, k, v = _rand(810, 2, 4, 6, 4, 2, 3)
+    slopes = np.array([[0.1, 0.5, 0.9, 1.3], [0.2, 0.6, 1.0, 1.4]])
+    o, lse = orc.fwd(q, k, v, False, 0.5, alibi=slopes)
+    for b in range(2):
+        for h in range(4):
+            ob, lb = orc.fwd(q[b:b + 1, :, h:h + 1], k[b:b + 1, :, h // 2:h // 2 + 1],
+                             v[b:b + 1, :, h // 2:h // 2 + 1], False, 0.5, alibi=[slopes[b, h]])
+            assert np.allclose(o[b, :, h], ob[0, :, 0], rtol=0, atol=TIGHT)
+            assert np.allclose(lse[b, h], lb[0, 0], rtol=0, atol=TIGHT)
+
+
+def check_alibi_as_extra_feature(orc):
+    # Where no visible key lies right of the diagonal (causal, or one decode query at the
+    # end), -slope |diag - j| = slope j - slope diag.  Appending 1 to q and slope j / scale
+    # to k_j makes plain attention add slope j to each score: O is the ALiBi O and the LSE
+    # exceeds the ALiBi LSE by slope * diag.  This goes through the pinned plain definition.
+    rng = np.random.default_rng(820)
+    for seed, (B, Sq, Sk, Hq, Hkv, d, causal) in enumerate(
+            ((1, 6, 6, 2, 1, 3, True), (2, 4, 9, 4, 2, 3, True), (2, 1, 12, 4, 2, 3, False),
+             (1, 7, 3, 2, 2, 2, True))):
+        q, k, v = _rand(830 + seed, B, Sq, Sk, Hq, Hkv, d)
+        slopes = rng.uniform(0.05, 1.0, (B, Hq))
+        scale = 0.7
+        o, lse = orc.fwd(q, k, v, causal, scale, alibi=slopes)
+        g = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                hk = h // g
+                qa = np.concatenate([q[b:b + 1, :, h:h + 1], np.ones((1, Sq, 1, 1))], axis=3)
+                feat = (slopes[b, h] * np.arange(Sk) / scale).reshape(1, Sk, 1, 1)
+                ka = np.concatenate([k[b:b + 1, :, hk:hk + 1], feat], axis=3)
+                va = np.concatenate([v[b:b + 1, :, hk:hk + 1], np.zeros((1, Sk, 1, 1))], axis=3)
+                oa, la = orc.fwd(qa, ka, va, causal, scale)
+                assert np.allclose(o[b, :, h], oa[0, :, 0, :d], rtol=0, atol=1e-11), (seed, b, h)
+                for i in range(Sq):
+                    if np.isneginf(la[0, 0, i]):
+                        assert np.isneginf(lse[b, h, i])
+                        continue
+                    diag = i + Sk - Sq
+                    assert abs(lse[b, h, i] - (la[0, 0, i] - slopes[b, h] * diag)) < 1e-11
+
+
+def check_softcap_closed_forms(orc):
+    g = golden("mask_variants.json")["derived"]["softcap"]
+    e = math.e
+    want_o, want_l = (2 + 6 * e) / (1 + e), math.log(1 + e)
+    q, k, v = one_row([g["q"]], [_num(x) for x in g["k"]], g["v"])
+    o, lse = orc.fwd(q, k, v, False, g["scale"], softcap=g["softcap"])
+    assert abs(o[0, 0, 0, 0] - want_o) < TIGHT and abs(lse[0, 0, 0] - want_l) < TIGHT
+    p = orc.probs(q, k, v, False, g["scale"], 0, 0, 0, softcap=g["softcap"])
+    assert np.allclose(p, [1 / (1 + e), e / (1 + e)], rtol=0, atol=TIGHT)
+    # The cap acts on the scaled score: the same logits through k = [0, 1], scale = ln 3.
+    q2, k2, v2 = one_row([1.0], [0.0, 1.0], g["v"])
+    o2, l2 = orc.fwd(q2, k2, v2, False, LN3, softcap=2.0)
+    assert abs(o2[0, 0, 0, 0] - want_o) < TIGHT and abs(l2[0, 0, 0] - want_l) < TIGHT
+    # Saturation: scores far above the cap all become the cap (equal weights) ...
+    q3, k3, v3 = one_row([1.0], [100.0, 200.0, 300.0], [1.0, 2.0, 6.0])
+    o3, l3 = orc.fwd(q3, k3, v3, False, 1.0, softcap=1.0)
+    assert abs(o3[0, 0, 0, 0] - 3.0) < TIGHT and abs(l3[0, 0, 0] - (1 + math.log(3))) < TIGHT
+    # ... and a cap far above the scores changes them by about s^3 / (3 c^2).
+    q4, k4, v4 = _rand(840, 1, 5, 7, 2, 1, 4)
+    _same(orc.fwd(q4, k4, v4, True, 0.5, softcap=1e7), orc.fwd(q4, k4, v4, True, 0.5), 1e-11)
+
+
+def check_variants_online_split_agree(orc):
+    rng = np.random.default_rng(850)
+    cases = ((1, 9, 9, 2, 1, 3, False, (2, 1), True, 0.0),
+             (2, 5, 11, 4, 2, 3, True, (3, -1), True, 3.0),
+             (1, 11, 4, 2, 2, 2, False, (1, 0), False, 1.5),
+             (2, 6, 6, 2, 1, 4, False, (-1, -1), True, 0.8),
+             (1, 8, 13, 2, 2, 3, False, (0, 2), False, 0.0))
+    for seed, (B, Sq, Sk, Hq, Hkv, d, causal, win, use_alibi, cap) in enumerate(cases):
+        q, k, v = _rand(860 + seed, B, Sq, Sk, Hq, Hkv, d)
+        opts = dict(window=win, alibi=rng.uniform(0.1, 0.9, (B, Hq)) if use_alibi else None,
+                    softcap=cap)
+        ref = orc.fwd(q, k, v, causal, 0.45, **opts)
+        for blk in (1, 2, 3, 5, 64):
+            _same(orc.online(q, k, v, causal, 0.45, blk, **opts), ref)
+        for blk, S in ((1, 4), (2, 3), (3, 2), (1, 9)):
+            _same(orc.split(q, k, v, causal, 0.45, blk, S, **opts)[2:], ref)
+        rows = [(B - 1, Hq - 1, Sq - 1), (0, 0, 0), (0, Hq // 2, Sq // 2)]
+        orow, lrow = orc.rows(q, k, v, causal, 0.45, rows, **opts)
+        for n, (b, h, i) in enumerate(rows):
+            assert np.array_equal(orow[n], ref[0][b, i, h]) and lrow[n] == ref[1][b, h, i]
+
+
+def decimal_attention_variants(q, k, v, causal, scale, window, slopes, cap):
+    """The variants in 50-digit decimal: scale, soft cap, ALiBi bias, window/causal mask."""
+    getcontext().prec = 50
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    g = Hq // Hkv
+    D = Decimal
+    o = np.zeros((B, Sq, Hq, d))
+    lse = np.zeros((B, Hq, Sq))
+    wl, wr = window
+
+    def tanh(x):
+        t = (2 * x).exp()
+        return (t - 1) / (t + 1)
+
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            for i in range(Sq):
+                diag = i + Sk - Sq
+                s = []
+                for j in range(Sk):
+                    if (causal and j > diag) or (wl >= 0 and j < diag - wl) or \
+                            (wr >= 0 and j > diag + wr):
+                        continue
+                    x = D(float(scale)) * sum(D(float(q[b, i, h, c])) * D(float(k[b, j, hk, c]))
+                                              for c in range(d))
+                    if cap > 0:
+                        x = D(cap) * tanh(x / D(cap))
+                    if slopes is not None:
+                        x -= D(float(slopes[b, h])) * abs(D(diag - j))
+                    s.append((j, x))
+                if not s:
+                    lse[b, h, i] = -np.inf
+                    continue
+                m = max(x for _, x in s)
+                w = [(j, (x - m).exp()) for j, x in s]
+                l = sum(x for _, x in w)
+                for c in range(d):
+                    o[b, i, h, c] = float(sum(x * D(float(v[b, j, hk, c])) for j, x in w) / l)
+                lse[b, h, i] = float(m + l.ln())
+    return o, lse
+
+
+def check_variants_decimal_brute_force(orc):
+    rng = np.random.default_rng(870)
+    for seed, (B, Sq, Sk, Hq, Hkv, d, causal, win, cap) in enumerate(
+            ((1, 5, 7, 2, 1, 3, False, (1, 2), 1.2), (1, 6, 6, 2, 2, 2, True, (2, -1), 0.0),
+             (2, 4, 3, 2, 1, 3, False, (-1, 0), 2.5), (1, 7, 5, 1, 1, 3, False, (0, 1), 0.7))):
+        q, k, v = _rand(880 + seed, B, Sq, Sk, Hq, Hkv, d)
+        slopes = rng.uniform(0.1, 1.5, (B, Hq))
+        od, ld = decimal_attention_variants(q, k, v, causal, 0.6, win, slopes, cap)
+        o, lse = orc.fwd(q, k, v, causal, 0.6, window=win, alibi=slopes, softcap=cap)
+        _same((o, lse), (od, ld))
+
+
+def check_variants_through_cache_and_varlen(orc):
+    # The per-batch helpers hand each batch its own slopes and the options.
+    rng = np.random.default_rng(890)
+    B, Sq, Hq, Hkv, d, page, nblk = 2, 3, 4, 2, 3, 4, 3
+    q = rng.standard_normal((B, Sq, Hq, d))
+    kc = rng.standard_normal((B * nblk, page, Hkv, d))
+    vc = rng.standard_normal((B * nblk, page, Hkv, d))
+    table = rng.permutation(B * nblk).reshape(B, nblk)
+    slopes = rng.uniform(0.1, 0.9, (B, Hq))
+    opts = dict(window=(4, 0), alibi=slopes, softcap=2.0)
+    o, lse = orc.kvcache(q, kc, vc, table, [10, 7], [1, 0], True, 0.7, **opts)
+    for b, (n, lp) in enumerate(((10, 1), (7, 0))):
+        kb, vb = orc.kv_gather(kc, vc, table, n, lp, b)
+        ob, lb = orc.fwd(q[b:b + 1], kb[None], vb[None], True, 0.7, window=(4, 0),
+                         alibi=slopes[b], softcap=2.0)
+        assert np.array_equal(o[b], ob[0]) and np.array_equal(lse[b], lb[0])
+    qv, kv, vv = (rng.standard_normal((9, Hq, d)), rng.standard_normal((11, Hkv, d)),
+                  rng.standard_normal((11, Hkv, d)))
+    o, lse = orc.varlen(qv, kv, vv, [0, 4, 9], [0, 5, 11], True, 0.7, **opts)
+    ob, lb = orc.fwd(qv[None, 4:9], kv[None, 5:11], vv[None, 5:11], True, 0.7, window=(4, 0),
+                     alibi=slopes[1], softcap=2.0)
+    assert np.array_equal(o[4:9], ob[0]) and np.array_equal(lse[:, 4:9], lb[0])
+
+
 ALL_CHECKS = [
     check_online_softmax_example, check_one_query_two_keys, check_exercise_1, check_exercise_2,
     check_causal_mask_pictures, check_tail_tile_case, check_special_cases,
@@ -536,6 +779,9 @@ ALL_CHECKS = [
     check_backward_finite_differences, check_backward_invariants, check_backward_units,
     check_backward_bf16_widening, check_varlen_printed_prefix_sums,
     check_varlen_equal_lengths_and_independence, check_paged_cache_gather, check_cache_append,
+    check_window_reductions, check_window_printed_range, check_alibi_derived_examples,
+    check_alibi_as_extra_feature, check_softcap_closed_forms, check_variants_online_split_agree,
+    check_variants_decimal_brute_force, check_variants_through_cache_and_varlen,
 ]
 
 

@@ -1,7 +1,7 @@
 """Mutation tests: plant each mistake the explainer's CPU-lab section asks about into a
 copy of the oracle (dropping alpha on the old numerator, dropping the scale, turning the
-causal <= into <), and a few plausible backward mistakes, rebuild it, and require at
-least one pin to fail."""
+causal <= into <), and a few plausible backward and mask/bias-variant mistakes, rebuild
+it, and require at least one pin to fail."""
 import os
 
 import pytest
@@ -11,8 +11,8 @@ import oracle_checks as oc
 
 MUTANTS = {
     "drop_alpha_on_numerator": ("o_row[c] = alpha * o_row[c] + pv;", "o_row[c] = o_row[c] + pv;"),
-    "drop_scale": ("return p->scale * acc;", "return acc;"),
-    "causal_strict": ("return j <= i + p->Sk - p->Sq;", "return j < i + p->Sk - p->Sq;"),
+    "drop_scale": ("double s = p->scale * acc;", "double s = acc;"),
+    "causal_strict": ("p->causal && !(j <= diag)", "p->causal && !(j < diag)"),
     # backward: the scale left out of dQ, D left out of dS, dS in place of P for dV,
     # dK with the wrong sign
     "bwd_drop_scale_dq": ("dq[q_index(&P, b, i, h, c)] = scale * acc;",
@@ -20,6 +20,19 @@ MUTANTS = {
     "bwd_ds_without_D": ("ds[j] = prob[j] * (dp - dsum_i);", "ds[j] = prob[j] * dp;"),
     "bwd_dv_uses_ds": ("dv[x] += prob[j] * doc;", "dv[x] += ds[j] * doc;"),
     "bwd_dk_sign": ("dk[x] += scale * ds[j] * qc;", "dk[x] -= scale * ds[j] * qc;"),
+    # mask and bias variants: window bounds off by one or mirrored, ALiBi with the wrong
+    # sign, without the absolute value or with the kv head's slope, the soft cap without
+    # its outer factor or applied before the scale
+    "window_left_inclusive": ("j < diag - p->window_left", "j <= diag - p->window_left"),
+    "window_right_mirrored": ("j > diag + p->window_right", "j > diag - p->window_right"),
+    "alibi_sign": ("s -= p->alibi[", "s += p->alibi["),
+    "alibi_no_abs": ("* fabs(dist);", "* dist;"),
+    "alibi_kv_head_slope": ("p->alibi[(int64_t)b * p->Hq + h]",
+                            "p->alibi[(int64_t)b * p->Hq + kv_head(p, h)]"),
+    "softcap_no_outer_factor": ("s = p->softcap * tanh(s / p->softcap);",
+                                "s = tanh(s / p->softcap);"),
+    "softcap_before_scale": ("double s = p->scale * acc;\n  if (p->softcap > 0.0) s = p->softcap * tanh(s / p->softcap);",
+                             "double s = acc;\n  if (p->softcap > 0.0) s = p->softcap * tanh(s / p->softcap);\n  s *= p->scale;"),
 }
 
 
