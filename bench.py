@@ -50,17 +50,31 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def visible_pairs(Sq, Sk, causal):
-    if not causal:
+def visible_pairs(Sq, Sk, causal, wl=-1, wr=-1):
+    """(query, key) pairs with j <= diag (causal) and diag - wl <= j <= diag + wr (window
+    limits >= 0), diag = i + Sk - Sq."""
+    if not causal and wl < 0 and wr < 0:
         return Sq * Sk
     total = 0
     for i in range(Sq):
-        total += max(0, min(Sk, i + Sk - Sq + 1))
+        diag = i + Sk - Sq
+        hi = Sk - 1
+        if causal:
+            hi = min(hi, diag)
+        if wr >= 0:
+            hi = min(hi, diag + wr)
+        lo = max(0, diag - wl) if wl >= 0 else 0
+        total += max(0, hi - lo + 1)
     return total
 
 
+def window_of(w):
+    return w.get("window_left", -1), w.get("window_right", -1)
+
+
 def prefill_flops(w):
-    return 4 * w["d"] * visible_pairs(w["Sq"], w["Sk"], w["causal"]) * w["B"] * w["Hq"]
+    return 4 * w["d"] * visible_pairs(w["Sq"], w["Sk"], w["causal"], *window_of(w)) * \
+        w["B"] * w["Hq"]
 
 
 def decode_bytes(w):
@@ -128,9 +142,15 @@ def run_prefill(torch, ff, name, steps, warmup):
     o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device="cuda:0")
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
+    wl, wr = window_of(w)
 
     def step():
-        ff.attn_fwd(qd, kd, vd, o, lse, B, Sq, Sk, Hq, Hkv, d, w["causal"], w["scale"], stream)
+        if wl < 0 and wr < 0:
+            ff.attn_fwd(qd, kd, vd, o, lse, B, Sq, Sk, Hq, Hkv, d, w["causal"], w["scale"],
+                        stream)
+        else:
+            ff.attn_fwd_ex(qd, kd, vd, o, lse, B, Sq, Sk, Hq, Hkv, d, w["causal"], wl, wr, None,
+                           0, 0.0, w["scale"], stream)
 
     for _ in range(warmup):
         step()
@@ -368,6 +388,9 @@ def describe(name):
                 "total_tokens": w["total"], "Hq": w["Hq"], "Hkv": w["Hkv"], "d": w["d"],
                 "causal": w["causal"], "parallelism": "none (1 GPU)"}
     label = name if name in synth.WORKLOADS else f"{name} (on {HEADLINE})"
+    wl, wr = window_of(w)
+    if wl >= 0 or wr >= 0:
+        kind += f" window ({wl}, {wr})"
     return {"workload": f"{label}: B={w['B']} Hq={w['Hq']} Hkv={w['Hkv']} Sq={w['Sq']} "
                         f"Sk={w['Sk']} d={w['d']} {kind}",
             "B": w["B"], "Sq": w["Sq"], "Sk": w["Sk"], "Hq": w["Hq"], "Hkv": w["Hkv"],

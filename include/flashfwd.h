@@ -55,7 +55,8 @@ typedef enum {
   FF_ERR_SPLITS = 6,   /* num_splits outside [1, FF_MAX_SPLITS] */
   FF_ERR_SCALE = 7,    /* scale not finite or not > 0 */
   FF_ERR_HIP = 8,      /* the HIP runtime reported an error (device query or launch) */
-  FF_ERR_ALIAS = 9     /* an output overlaps an input */
+  FF_ERR_ALIAS = 9,    /* an output overlaps an input */
+  FF_ERR_OPTION = 10   /* a mask/bias option out of range (the _ex entry points) */
 } ff_status;
 
 #define FF_MAX_SPLITS 128
@@ -71,6 +72,29 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
              int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal, float scale,
              void* stream);
+
+/* attn_fwd with the mask and bias variants ("flash attention V2 code walk-through", the
+ * split-KV kernel's template flags Is_local, Has_alibi and Is_softcap, and its
+ * n_block_min / n_block_max clipping).  With diag = i + Sk - Sq, the key aligned with
+ * query row i:
+ *   window_left, window_right: key j is visible iff
+ *     diag - window_left <= j <= diag + window_right; -1 means no limit on that side.
+ *     With causal set, j <= diag holds as well (causal is the window (-1, 0)).
+ *   alibi_slopes: NULL, or fp32 device slopes; query head h of batch b uses
+ *     alibi_slopes[b * alibi_batch_stride + h] (alibi_batch_stride 0: one slope per head,
+ *     [Hq]; Hq: one per batch and head, [B, Hq]).  -slope * |diag - j| is added to the
+ *     score of key j.
+ *   softcap: 0 for none; c > 0 maps each scaled score s to c * tanh(s / c) before the
+ *     ALiBi bias and the mask (the page gives no formula; this is the plain tanh limit).
+ * The LSE is the logsumexp of the resulting logits.  With no option set (windows -1,
+ * no slopes, softcap 0) this is attn_fwd, bit for bit.  A row whose window holds no key
+ * gets O = 0, LSE = -inf.  Errors: FF_ERR_OPTION for a window below -1, a negative or
+ * non-finite softcap, or a batch stride other than 0 or Hq; FF_ERR_ALIGN for slopes not
+ * 4-byte aligned; FF_ERR_ALIAS if an output overlaps the slopes; otherwise as attn_fwd. */
+int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse,
+                int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
+                int window_left, int window_right, const float* alibi_slopes,
+                int alibi_batch_stride, float softcap, float scale, void* stream);
 
 /* Forward over a variable-length batch ("03 forward CUDA kernel" section 8: sequences
  * concatenated without padding, boundaries given by prefix sums; "flash attention V2
@@ -160,6 +184,20 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
                      int Hq, int Hkv, int d, int num_blocks, int page_size,
                      int max_blocks_per_seq, int new_keys, int causal, float scale,
                      int num_splits, void* stream);
+
+/* attn_fwd_kvcache with the mask and bias variants of attn_fwd_ex.  diag = i + n_b - Sq
+ * for batch b, with n_b = cache_seqlens[b] + new_keys its key count (positions left of
+ * cache_leftpad[b] stay invisible).  The window narrows the keys the splits share, so
+ * num_splits splits cover only the visible range.  Arguments, errors and outputs
+ * otherwise as attn_fwd_kvcache and attn_fwd_ex. */
+int attn_fwd_kvcache_ex(const void* q, const void* k_cache, const void* v_cache,
+                        const int* cache_seqlens, const int* cache_leftpad,
+                        const int* block_table, float* o_accum, float* lse_accum, float* o,
+                        float* lse, int B, int Sq, int Hq, int Hkv, int d, int num_blocks,
+                        int page_size, int max_blocks_per_seq, int new_keys, int causal,
+                        int window_left, int window_right, const float* alibi_slopes,
+                        int alibi_batch_stride, float softcap, float scale, int num_splits,
+                        void* stream);
 
 /* In-place append of new keys and values to a cache ("03 forward CUDA kernel" section 8;
  * the walk-through's Append_KV case, new k/v given as knew/vnew): k_new[b][t] and

@@ -121,4 +121,18 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 
 __device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
 
+// Mask and bias variants of the forward kernels (their VAR template argument), after the
+// walk-through's Is_local, Has_alibi and Is_softcap flags: the sliding window (window
+// limits of -1 mask nothing), the ALiBi bias and the soft cap.  VAR = 0 is the plain
+// kernel; any variant kernel includes the window.
+constexpr int kVarWindow = 1, kVarAlibi = 2, kVarSoftcap = 4;
+
+// Soft-capped logit in base-2 units, c log2(e) tanh(y) with y = s scale / c, from
+// tanh(y) = 1 - 2 / (e^(2y) + 1) and e^(2y) = 2^(s k), k = 2 scale log2(e) / c;
+// cap2 = c log2(e).  The limits come out exact: e^(2y) = inf gives cap2, 0 gives -cap2.
+__device__ __forceinline__ float softcap2(float s, float k, float cap2) {
+  const float e = fast_exp2(s * k);
+  return __builtin_fmaf(__builtin_amdgcn_rcpf(e + 1.f), -2.f * cap2, cap2);
+}
+
 }  // namespace ff

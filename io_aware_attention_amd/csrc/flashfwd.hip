@@ -109,6 +109,50 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? FF_OK : FF_ERR_HIP;
 }
 
+// Mask and bias options of the _ex entry points, checked, with the variant kernel that
+// serves them (0 = none set: the plain kernel).
+struct Variant {
+  int wl = -1, wr = -1;
+  const float* alibi = nullptr;
+  int alibi_bstride = 0;
+  float softcap = 0.f;
+  int var = 0;
+};
+
+int check_variant(int window_left, int window_right, const float* alibi_slopes,
+                  int alibi_batch_stride, float softcap, int Hq, Variant* v) {
+  if (window_left < -1 || window_right < -1) return FF_ERR_OPTION;
+  if (!isfinite(softcap) || softcap < 0.f) return FF_ERR_OPTION;
+  if (alibi_slopes && alibi_batch_stride != 0 && alibi_batch_stride != Hq) return FF_ERR_OPTION;
+  if (alibi_slopes && ((uintptr_t)alibi_slopes & 3u)) return FF_ERR_ALIGN;
+  v->wl = window_left;
+  v->wr = window_right;
+  v->alibi = alibi_slopes;
+  v->alibi_bstride = alibi_slopes ? alibi_batch_stride : 0;
+  v->softcap = softcap;
+  const bool any = window_left >= 0 || window_right >= 0 || alibi_slopes || softcap > 0.f;
+  v->var = any ? ff::kVarWindow | (alibi_slopes ? ff::kVarAlibi : 0) |
+                     (softcap > 0.f ? ff::kVarSoftcap : 0)
+               : 0;
+  return FF_OK;
+}
+
+// The slopes an ALiBi call reads: [B, Hq] or [Hq].
+int64_t alibi_bytes(const Variant& v, int B, int Hq) {
+  if (!v.alibi) return 0;
+  return (v.alibi_bstride ? (int64_t)B * Hq : (int64_t)Hq) * 4;
+}
+
+template <typename P>
+void set_variant(P& p, const Variant& v, float scale) {
+  p.wl = v.wl;
+  p.wr = v.wr;
+  p.alibi = v.alibi;
+  p.alibi_bstride = v.alibi_bstride;
+  p.cap_k = v.softcap > 0.f ? 2.f * scale * ff::kLog2e / v.softcap : 0.f;
+  p.cap2 = v.softcap * ff::kLog2e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,6 +169,9 @@ const char* attn_status_string(int status) {
     case FF_ERR_SCALE: return "scale must be finite and positive";
     case FF_ERR_HIP: return "HIP runtime error";
     case FF_ERR_ALIAS: return "an output buffer overlaps another buffer";
+    case FF_ERR_OPTION:
+      return "invalid mask/bias option (window < -1, softcap < 0 or not finite, "
+             "or ALiBi batch stride not 0 or Hq)";
     default: return "unknown status";
   }
 }
@@ -212,9 +259,32 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
 
 namespace {
 
+template <int D, bool CAUSAL>
+void launch_prefill_var(int var, dim3 grid, dim3 block, hipStream_t s, const ff::FwdParams& p) {
+  using namespace ff;
+  switch (var) {
+    case 0: hipLaunchKernelGGL((attn_fwd_prefill<D, CAUSAL, 0>), grid, block, 0, s, p); break;
+    case kVarWindow:
+      hipLaunchKernelGGL((attn_fwd_prefill<D, CAUSAL, kVarWindow>), grid, block, 0, s, p);
+      break;
+    case kVarWindow | kVarAlibi:
+      hipLaunchKernelGGL((attn_fwd_prefill<D, CAUSAL, kVarWindow | kVarAlibi>), grid, block, 0,
+                         s, p);
+      break;
+    case kVarWindow | kVarSoftcap:
+      hipLaunchKernelGGL((attn_fwd_prefill<D, CAUSAL, kVarWindow | kVarSoftcap>), grid, block,
+                         0, s, p);
+      break;
+    default:
+      hipLaunchKernelGGL((attn_fwd_prefill<D, CAUSAL, kVarWindow | kVarAlibi | kVarSoftcap>),
+                         grid, block, 0, s, p);
+      break;
+  }
+}
+
 // Fills the work-list fields of p (B, Sq = longest query sequence, Hq, Hkv set) and
-// launches the prefill kernel.
-int launch_prefill(ff::FwdParams& p, int d, int causal, float scale, void* stream) {
+// launches the prefill kernel (the variant kernel var; p's variant fields set).
+int launch_prefill(ff::FwdParams& p, int d, int causal, float scale, void* stream, int var = 0) {
   p.G = p.Hq / p.Hkv;
   p.num_m = (int)cdiv(p.Sq, ff::PrefillTraits<128>::BM);
   p.u_per = (int)cdiv((int64_t)p.B * p.Hkv, 8);
@@ -225,21 +295,18 @@ int launch_prefill(ff::FwdParams& p, int d, int causal, float scale, void* strea
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
   if (d == 128) {
-    if (causal) hipLaunchKernelGGL((ff::attn_fwd_prefill<128, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((ff::attn_fwd_prefill<128, false>), grid, block, 0, s, p);
+    if (causal) launch_prefill_var<128, true>(var, grid, block, s, p);
+    else launch_prefill_var<128, false>(var, grid, block, s, p);
   } else {
-    if (causal) hipLaunchKernelGGL((ff::attn_fwd_prefill<64, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((ff::attn_fwd_prefill<64, false>), grid, block, 0, s, p);
+    if (causal) launch_prefill_var<64, true>(var, grid, block, s, p);
+    else launch_prefill_var<64, false>(var, grid, block, s, p);
   }
   return launch_status();
 }
 
-}  // namespace
-
-extern "C" {
-
-int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Sq,
-             int Sk, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+int fwd_dense(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Sq,
+              int Sk, int Hq, int Hkv, int d, int causal, float scale, const Variant& var,
+              void* stream) {
   if (!q || !k || !v || !o || !lse) return FF_ERR_NULL;
   int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
   if (st) return st;
@@ -249,6 +316,8 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, 
   const void* outs[2] = {o, lse};
   const int64_t ob[2] = {(int64_t)B * Sq * Hq * d * 4, (int64_t)B * Hq * Sq * 4};
   if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 2))) return st;
+  for (int i = 0; i < 2; ++i)
+    if (overlaps(outs[i], ob[i], var.alibi, alibi_bytes(var, B, Hq))) return FF_ERR_ALIAS;
 
   ff::FwdParams p = {};
   p.q = (const uint16_t*)q;
@@ -262,7 +331,28 @@ int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, 
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.cu_q = p.cu_k = nullptr;
-  return launch_prefill(p, d, causal, scale, stream);
+  set_variant(p, var, scale);
+  return launch_prefill(p, d, causal, scale, stream, var.var);
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Sq,
+             int Sk, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  return fwd_dense(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, Variant{}, stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, float* o, float* lse, int B,
+                int Sq, int Sk, int Hq, int Hkv, int d, int causal, int window_left,
+                int window_right, const float* alibi_slopes, int alibi_batch_stride,
+                float softcap, float scale, void* stream) {
+  Variant var;
+  int st = check_variant(window_left, window_right, alibi_slopes, alibi_batch_stride, softcap,
+                         Hq, &var);
+  if (st) return st;
+  return fwd_dense(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, var, stream);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, float* o, float* lse,
@@ -364,7 +454,7 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o_accum
     if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 2))) return st;
   }
 
-  ff::SplitParams p;
+  ff::SplitParams p = {};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
   p.v = (const uint16_t*)v;
@@ -389,17 +479,44 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o_accum
   if (total >= kMaxElems) return FF_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
-  if (d == 128) hipLaunchKernelGGL((ff::attn_fwd_splitkv<128, false>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((ff::attn_fwd_splitkv<64, false>), grid, block, 0, s, p);
+  if (d == 128) hipLaunchKernelGGL((ff::attn_fwd_splitkv<128, false, 0>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((ff::attn_fwd_splitkv<64, false, 0>), grid, block, 0, s, p);
   return launch_status();
 }
 
-int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
-                     const int* cache_seqlens, const int* cache_leftpad, const int* block_table,
-                     float* o_accum, float* lse_accum, float* o, float* lse, int B, int Sq,
-                     int Hq, int Hkv, int d, int num_blocks, int page_size,
-                     int max_blocks_per_seq, int new_keys, int causal, float scale,
-                     int num_splits, void* stream) {
+}  // extern "C"
+
+namespace {
+
+template <int D>
+void launch_cache_var(int var, dim3 grid, dim3 block, hipStream_t s, const ff::SplitParams& p) {
+  using namespace ff;
+  switch (var) {
+    case 0: hipLaunchKernelGGL((attn_fwd_splitkv<D, true, 0>), grid, block, 0, s, p); break;
+    case kVarWindow:
+      hipLaunchKernelGGL((attn_fwd_splitkv<D, true, kVarWindow>), grid, block, 0, s, p);
+      break;
+    case kVarWindow | kVarAlibi:
+      hipLaunchKernelGGL((attn_fwd_splitkv<D, true, kVarWindow | kVarAlibi>), grid, block, 0, s,
+                         p);
+      break;
+    case kVarWindow | kVarSoftcap:
+      hipLaunchKernelGGL((attn_fwd_splitkv<D, true, kVarWindow | kVarSoftcap>), grid, block, 0,
+                         s, p);
+      break;
+    default:
+      hipLaunchKernelGGL((attn_fwd_splitkv<D, true, kVarWindow | kVarAlibi | kVarSoftcap>), grid,
+                         block, 0, s, p);
+      break;
+  }
+}
+
+int fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                const int* cache_seqlens, const int* cache_leftpad, const int* block_table,
+                float* o_accum, float* lse_accum, float* o, float* lse, int B, int Sq, int Hq,
+                int Hkv, int d, int num_blocks, int page_size, int max_blocks_per_seq,
+                int new_keys, int causal, float scale, int num_splits, const Variant& var,
+                void* stream) {
   if (!q || !k_cache || !v_cache || !cache_seqlens) return FF_ERR_NULL;
   if (num_splits < 1 || num_splits > FF_MAX_SPLITS) return FF_ERR_SPLITS;
   if (num_splits == 1 && (!o || !lse)) return FF_ERR_NULL;
@@ -433,9 +550,11 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
     ob[0] = num_splits * rows_all * d * 4, ob[1] = num_splits * rows_all * 4;
   }
   if (overlaps(outs[0], ob[0], outs[1], ob[1])) return FF_ERR_ALIAS;
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(outs[i], ob[i], ins[j], in_b[j])) return FF_ERR_ALIAS;
+    if (overlaps(outs[i], ob[i], var.alibi, alibi_bytes(var, B, Hq))) return FF_ERR_ALIAS;
+  }
 
   ff::SplitParams p = {};
   p.q = (const uint16_t*)q;
@@ -464,13 +583,46 @@ int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
   p.page = page_size;
   p.max_blocks = block_table ? max_blocks_per_seq : 1;
   p.new_keys = new_keys;
+  set_variant(p, var, scale);
   const int64_t total = (int64_t)B * Hkv * p.num_mb * num_splits;
   if (total >= kMaxElems) return FF_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
-  if (d == 128) hipLaunchKernelGGL((ff::attn_fwd_splitkv<128, true>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((ff::attn_fwd_splitkv<64, true>), grid, block, 0, s, p);
+  if (d == 128) launch_cache_var<128>(var.var, grid, block, s, p);
+  else launch_cache_var<64>(var.var, grid, block, s, p);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                     const int* cache_seqlens, const int* cache_leftpad, const int* block_table,
+                     float* o_accum, float* lse_accum, float* o, float* lse, int B, int Sq,
+                     int Hq, int Hkv, int d, int num_blocks, int page_size,
+                     int max_blocks_per_seq, int new_keys, int causal, float scale,
+                     int num_splits, void* stream) {
+  return fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, o_accum,
+                     lse_accum, o, lse, B, Sq, Hq, Hkv, d, num_blocks, page_size,
+                     max_blocks_per_seq, new_keys, causal, scale, num_splits, Variant{}, stream);
+}
+
+int attn_fwd_kvcache_ex(const void* q, const void* k_cache, const void* v_cache,
+                        const int* cache_seqlens, const int* cache_leftpad,
+                        const int* block_table, float* o_accum, float* lse_accum, float* o,
+                        float* lse, int B, int Sq, int Hq, int Hkv, int d, int num_blocks,
+                        int page_size, int max_blocks_per_seq, int new_keys, int causal,
+                        int window_left, int window_right, const float* alibi_slopes,
+                        int alibi_batch_stride, float softcap, float scale, int num_splits,
+                        void* stream) {
+  Variant var;
+  int st = check_variant(window_left, window_right, alibi_slopes, alibi_batch_stride, softcap,
+                         Hq, &var);
+  if (st) return st;
+  return fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, o_accum,
+                     lse_accum, o, lse, B, Sq, Hq, Hkv, d, num_blocks, page_size,
+                     max_blocks_per_seq, new_keys, causal, scale, num_splits, var, stream);
 }
 
 int attn_kvcache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -30,6 +30,14 @@
 // (base-2 units); numerator and denominator always share it, so the result is
 // the same up to rounding (the explainer's rescaling-invariance argument) while
 // the O rescale is skipped for almost every tile.
+//
+// Variants (VAR != 0; the walk-through's Is_local, Has_alibi, Is_softcap).  With
+// diag = i + Sk - Sq, key j is visible to query i iff diag - wl <= j <= diag + wr
+// (-1: no limit), on top of the causal limit.  The window clips the key-tile range at
+// both ends (the walk-through's n_block_min / n_block_max), so tiles are masked at the
+// top (right edge, visited first) and at the bottom (left edge, visited last).  With
+// ALiBi or the soft cap, each score is turned into its base-2 logit before the row
+// maximum: the cap c log2(e) tanh(s scale / c), then the bias -slope |diag - j| log2(e).
 #pragma once
 #include <utility>
 
@@ -54,6 +62,13 @@ struct FwdParams {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  // Variants: window limits (-1 = none); ALiBi slope of (batch b, head h) at
+  // alibi[b * alibi_bstride + h]; soft-cap constants cap_k = 2 scale log2(e) / c and
+  // cap2 = c log2(e).
+  int wl, wr;
+  const float* alibi;
+  int alibi_bstride;
+  float cap_k, cap2;
 };
 
 // Rows [start, start + len) of sequence b under prefix sums cu (clamped to [0, total],
@@ -122,9 +137,11 @@ struct PrefillTraits {
   static __device__ __forceinline__ int vkey(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist for the device target only
+  constexpr bool WIN = VAR & kVarWindow, ALIBI = VAR & kVarAlibi, CAP = VAR & kVarSoftcap;
+  constexpr bool LOGIT = ALIBI || CAP;  // scores become base-2 logits before the row max
   using T = PrefillTraits<D>;
   constexpr int BM = T::BM, BN = T::BN, ROWB = T::ROWB, CPR = T::CPR, TILE = T::TILE;
   constexpr int LOADS = T::LOADS;
@@ -188,12 +205,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     const int tm = first <= 0 ? 0 : first / BN;
     n_mask_lo = tm < n_mask_lo ? tm : n_mask_lo;
   }
+  // Window: tiles [n_min, n_max) hold keys some row of the tile sees; tiles below n_bot
+  // hold keys left of the last row's window and need the element mask too.
+  int n_min = 0, n_bot = 0;
+  if constexpr (WIN) {
+    // 64-bit positions (a window may reach past 2^31); tile numbers by shifts, which stay
+    // scalar, of non-negative values
+    constexpr int LB = __builtin_ctz(BN);
+    static_assert((1 << LB) == BN, "BN must be a power of two");
+    if (p.wr >= 0) {
+      const int64_t lim = (int64_t)last_q + Sk - Sq + p.wr;  // right limit of the last row
+      const int64_t nm = lim < 0 ? 0 : (lim >> LB) + 1;
+      n_max = nm < n_max ? (int)nm : n_max;
+      const int64_t first = (int64_t)q0 + Sk - Sq + p.wr + 1;  // first key row q0 misses
+      const int64_t tm = first <= 0 ? 0 : first >> LB;
+      n_mask_lo = tm < n_mask_lo ? (int)tm : n_mask_lo;
+    }
+    if (p.wl >= 0) {
+      const int64_t lo_first = (int64_t)q0 + Sk - Sq - p.wl;    // left limit of row q0
+      const int64_t lo_last = (int64_t)last_q + Sk - Sq - p.wl; // left limit of the last row
+      n_min = lo_first <= 0 ? 0 : (int)(lo_first >> LB);
+      const int64_t nb = lo_last <= 0 ? 0 : (lo_last + BN - 1) >> LB;
+      n_bot = (int)(nb < n_max ? nb : n_max);
+      n_bot = n_bot > n_min ? n_bot : n_min;
+    }
+  }
 
   const int64_t q_stride = (int64_t)p.Hq * D;    // elements between query positions
   const int kv_row_bytes = p.Hkv * D * 2;        // bytes between key positions
   const float c2 = p.scale_log2;
 
-  if (n_max <= 0) {  // no visible key for any row of this tile
+  if (n_max <= n_min) {  // no visible key for any row of this tile
     if (qrow < Sq) {
       float* orow = p.o + ((int64_t)q_start + qrow) * q_stride + (int64_t)h * D;
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -237,12 +279,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   auto par = [&](int t) { return (n_max - 1 - t) & 1; };
   auto kbuf = [&](int t) { return smem_addr + par(t) * TILE; };
   auto vbuf = [&](int t) { return smem_addr + (2 + par(t)) * TILE; };
-  // Loads of tile t of K (or V) into its buffer.  A tile index below 0 gets an empty
-  // descriptor: every lane reads as out of range, and the buffer is not read later.
+  // Loads of tile t of K (or V) into its buffer.  A tile index below the range (below 0,
+  // or below the window's first tile) gets an empty descriptor: every lane reads as out of
+  // range, and the buffer is not read later.
+  const int n_lo = WIN ? __builtin_amdgcn_readfirstlane(n_min) : 0;  // wave-uniform
   auto issue = [&](const char* base, const int* off, int t, uint32_t lds) {
-    const int rows_left = t >= 0 ? Sk - t * BN : 0;
+    const int rows_left = t >= n_lo ? Sk - t * BN : 0;
     const uint32_t bytes = (uint32_t)rows_left * (uint32_t)kv_row_bytes;
-    const int64_t toff = t >= 0 ? (int64_t)t * BN * kv_row_bytes : 0;
+    const int64_t toff = t >= n_lo ? (int64_t)t * BN * kv_row_bytes : 0;
     const i32x4 rd = buffer_desc(base + toff, bytes);
     const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds + 1024 * LOADS * wave);
 #pragma unroll
@@ -297,13 +341,33 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     const int j = (e & 15) >> 2, i = e & 3;
     return 32 * (e >> 4) + 16 * (j >> 1) + 4 * (j & 1) + i;
   };
-  const int last_key = CAUSAL && qrow + Sk - Sq < Sk - 1 ? qrow + Sk - Sq : Sk - 1;
+  int last_key = CAUSAL && qrow + Sk - Sq < Sk - 1 ? qrow + Sk - Sq : Sk - 1;
+  int first_key = 0;  // window: keys below are invisible to this row
+  if constexpr (WIN) {
+    const int64_t diag = (int64_t)qrow + Sk - Sq;
+    if (p.wr >= 0 && diag + p.wr < last_key) last_key = (int)(diag + p.wr);
+    if (p.wl >= 0 && diag - p.wl > 0) first_key = (int)(diag - p.wl);
+  }
   auto vis_lim = [&](int t) { return last_key - t * BN - 8 * H; };
+  auto vis_lo = [&](int t) { return first_key - t * BN - 8 * H; };
+  // The window's bottom tiles: key_off(e) < vis_lo(t) is invisible as well.
   auto mask = [&](f32x16* sc, int t) {
     const int vl = vis_lim(t);
+    const int vlo = vis_lo(t);
 #pragma unroll
     for (int e = 0; e < 32; ++e)
-      if (key_off(e) > vl) sc[e >> 4][e & 15] = -INFINITY;
+      if (key_off(e) > vl || (WIN && key_off(e) < vlo)) sc[e >> 4][e & 15] = -INFINITY;
+  };
+  // Variants: score -> base-2 logit (soft cap, then ALiBi bias).  rb = diag - (first key
+  // of this lane's half of tile t), so key_off(e) is at distance rb - key_off(e).
+  const float slope2 = ALIBI ? p.alibi[(int64_t)b * p.alibi_bstride + h] * kLog2e : 0.f;
+  auto rbase = [&](int t) { return (float)(qrow + Sk - Sq - t * BN - 8 * H); };
+  auto logit = [&](float s, int e, float rb) {
+    float x;
+    if constexpr (CAP) x = softcap2(s, p.cap_k, p.cap2);
+    else x = s * c2;
+    if constexpr (ALIBI) x = __builtin_fmaf(-slope2, __builtin_fabsf(rb - (float)key_off(e)), x);
+    return x;
   };
   // Row maximum of a score tile in scale*log2(e) units (both wave halves).
   auto rowmax = [&](const f32x16* sc) {
@@ -312,8 +376,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = vmax(mx, sc[kb][e]);
-    return max_xor32(mx) * c2;
+    return LOGIT ? max_xor32(mx) : max_xor32(mx) * c2;
   };
+  const float cexp = LOGIT ? 1.f : c2;  // exponent factor of the stored scores
   // ---- software-pipelined key loop, tiles n_max-1 down to 0.  While tile t's
   // softmax and PV product run, tile t-1's QK^T product is issued (K streams one
   // tile ahead of V) and its row maximum is taken in the shadow of tile t's PV
@@ -337,7 +402,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   // S[P ^ 1] receives tile t-1's; the roles swap every step, so nothing is copied.
   f32x16 S[2][2];
   gemm0(kbuf(t), S[0]);
-  if (t >= n_mask_lo) mask(S[0], t);
+  if constexpr (LOGIT) {
+    const float rb = rbase(t);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) S[0][e >> 4][e & 15] = logit(S[0][e >> 4][e & 15], e, rb);
+  }
+  if (t >= n_mask_lo || t < n_bot) mask(S[0], t);
   float mx = rowmax(S[0]);
 
   // One step (parity P): softmax + PV of tile t; QK^T, mask and row max of tile t-1
@@ -396,7 +466,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
 #pragma unroll
       for (int q = 0; q < EPG; ++q) {
         const int e = i * EPG + q;  // 0..31: block e / 16, element e % 16
-        const float x = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], c2, -m_use));
+        const float x = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], cexp, -m_use));
         sc[e >> 4][e & 15] = x;
         lsum[q & 3] += x;
       }
@@ -416,6 +486,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
     gemm1_read<0, D, ROWB>(vl, va, flo[0], fhi[0]);
     gemm1_read<1, D, ROWB>(vl, va, flo[1], fhi[1]);
     const int vln = vis_lim(t - 1);
+    const int vlon = vis_lo(t - 1);
+    const float rbn = LOGIT ? rbase(t - 1) : 0.f;
     float mxn = -INFINITY;
     static_for<NG1>([&](auto I) {
       constexpr int i = decltype(I)::value;
@@ -428,8 +500,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
 #pragma unroll
         for (int q = 0; q < EPG; ++q) {
           const int e = i * EPG + q;
+          if constexpr (LOGIT) sn[e >> 4][e & 15] = logit(sn[e >> 4][e & 15], e, rbn);
           if constexpr (MASK_NEXT) {
-            if (key_off(e) > vln) sn[e >> 4][e & 15] = -INFINITY;
+            if (key_off(e) > vln || (WIN && key_off(e) < vlon)) sn[e >> 4][e & 15] = -INFINITY;
           }
           mxn = vmax(mxn, sn[e >> 4][e & 15]);
         }
@@ -437,36 +510,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (HAS_NEXT) {
-      mx = max_xor32(mxn) * c2;
+      mx = LOGIT ? max_xor32(mxn) : max_xor32(mxn) * c2;
       wait_vmem();
       __syncthreads();
     }
   };
   // The loop runs in pairs of steps (parity 0, then 1).  Masked tiles (key tail,
-  // causal diagonal) are the first ones visited: steps t with t - 1 >= n_mask_lo mask
-  // the next tile, and their number is rounded up to even (masking a tile that needs
-  // none changes nothing), so every pair loop starts at parity 0 and the mask code
-  // stays out of the main loop.
+  // causal diagonal, window right edge) are the first ones visited: steps t with
+  // t - 1 >= n_mask_lo mask the next tile, and their number is rounded up to even
+  // (masking a tile that needs none changes nothing), so every pair loop starts at
+  // parity 0 and the mask code stays out of the main loop.  The window's left-edge tiles
+  // (below n_bot) come last, again in masked pairs.
   using Par0 = std::integral_constant<int, 0>;
   using Par1 = std::integral_constant<int, 1>;
   using Yes = MaskTag<true>;
   using No = MaskTag<false>;
-  const int n_next = n_max - 1;  // steps that have a next tile
-  int n_masked = n_next - (n_mask_lo > 0 ? n_mask_lo : 0);
+  const int n_next = n_max - 1 - n_min;  // steps that have a next tile
+  int n_masked = n_next - (n_mask_lo > n_min ? n_mask_lo - n_min : 0);
   n_masked = n_masked < 0 ? 0 : (n_masked > n_next ? n_next : n_masked);
-  for (int pair = 0; pair < (n_masked + 1) / 2 && t >= 2; ++pair, t -= 2) {
+  for (int pair = 0; pair < (n_masked + 1) / 2 && t - n_min >= 2; ++pair, t -= 2) {
     step(Par0{}, t, Yes{}, Yes{});
     step(Par1{}, t - 1, Yes{}, Yes{});
   }
-  for (; t >= 2; t -= 2) {
+  for (; t - 2 >= n_bot; t -= 2) {  // both next tiles lie at or above n_bot
     step(Par0{}, t, Yes{}, No{});
     step(Par1{}, t - 1, Yes{}, No{});
   }
-  if (t == 1) {
-    step(Par0{}, 1, Yes{}, Yes{});
-    step(Par1{}, 0, No{}, No{});
+  if constexpr (WIN) {
+    for (; t - n_min >= 2; t -= 2) {
+      step(Par0{}, t, Yes{}, Yes{});
+      step(Par1{}, t - 1, Yes{}, Yes{});
+    }
+  }
+  if (t - n_min == 1) {
+    step(Par0{}, n_min + 1, Yes{}, Yes{});
+    step(Par1{}, n_min, No{}, No{});
   } else {
-    step(Par0{}, 0, No{}, No{});
+    step(Par0{}, n_min, No{}, No{});
   }
 
   // ---- epilogue: O = o / l, LSE = (m + log2 l) ln 2

@@ -18,6 +18,12 @@
 // eight scores are eight consecutive keys, which makes them the P^T operand
 // as they stand.  V goes through a per-wavefront LDS area, transposed on the
 // way in, so V^T fragments are single 128-bit LDS reads.
+//
+// Variants (VAR != 0, cache kernels only; the walk-through's Is_local, Has_alibi,
+// Is_softcap): with diag = i + Sk - Sq for query i, the window keeps keys
+// diag - wl <= j <= diag + wr (-1: no limit) and narrows the keys the splits share;
+// ALiBi adds -slope |diag - j| and the soft cap maps s to c tanh(s scale / c), both
+// applied to the scores in base-2 units before the row maximum.
 #pragma once
 #include "device.h"
 
@@ -47,6 +53,13 @@ struct SplitParams {
   const int* leftpad;
   const int* block_table;
   int num_blocks, page, max_blocks, new_keys;
+  // Variants: window limits (-1 = none); ALiBi slope of (batch b, query head h) at
+  // alibi[b * alibi_bstride + h]; soft-cap constants cap_k = 2 scale log2(e) / c and
+  // cap2 = c log2(e).
+  int wl, wr;
+  const float* alibi;
+  int alibi_bstride;
+  float cap_k, cap2;
 };
 
 // Wavefront-local LDS handoff: the lanes of one wavefront exchange data through
@@ -70,9 +83,12 @@ struct SplitTraits {
   static constexpr int kLds = kWaves * WV > kCombine ? kWaves * WV : kCombine;
 };
 
-template <int D, bool CACHE>
+template <int D, bool CACHE, int VAR>
 __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist for the device target only
+  constexpr bool WIN = VAR & kVarWindow, ALIBI = VAR & kVarAlibi, CAP = VAR & kVarSoftcap;
+  constexpr bool LOGIT = ALIBI || CAP;  // scores become base-2 logits before the row max
+  static_assert(VAR == 0 || CACHE, "variants are built for the cache kernel");
   using T = SplitTraits<D>;
   constexpr int TK = T::TK, VS = T::VS, VB = T::VB, NW = T::kWaves;
   __shared__ __attribute__((aligned(16))) char smem[T::kLds];
@@ -110,31 +126,64 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   const int qh = hk * G + R % G;
 
   // key range of this split, clipped by the causal limit of the block's last row
+  const int r_last = (mb * 16 + 16 < p.rows ? mb * 16 + 16 : p.rows) - 1;
+  const int i_first = (mb * 16) / G;
+  int k_first = lp, k_end = Sk;  // keys some row of the block may see
+  int mask_below = lp;           // steps starting below this need the element mask
+  if constexpr (WIN) {
+    const int64_t off = (int64_t)Sk - Sq;
+    if (p.wr >= 0) {
+      const int64_t e = (int64_t)(r_last / G) + off + p.wr + 1;
+      k_end = e < k_end ? (e < 0 ? 0 : (int)e) : k_end;
+    }
+    if (p.wl >= 0) {
+      const int64_t f = (int64_t)i_first + off - p.wl;
+      const int64_t fl = (int64_t)(r_last / G) + off - p.wl;
+      k_first = f > k_first ? (int)(f < Sk ? f : Sk) : k_first;
+      mask_below = fl > mask_below ? (int)(fl < Sk ? fl : Sk) : mask_below;
+    }
+  }
   int j_lo, j_hi;
   if constexpr (CACHE) {
     // equal shares of whole 128-key blocks from the step holding the first key
-    const int base0 = lp & ~(TK - 1);
-    const int per = (Sk - base0 + p.num_splits - 1) / p.num_splits;
+    const int base0 = k_first & ~(TK - 1);
+    int per = (k_end - base0 + p.num_splits - 1) / p.num_splits;
+    per = per < 0 ? 0 : per;
     const int chunk = (per + NW * TK - 1) / (NW * TK) * (NW * TK);
     j_lo = base0 + s * chunk;
-    j_hi = j_lo + chunk < Sk ? j_lo + chunk : Sk;
+    j_hi = j_lo + chunk < k_end ? j_lo + chunk : k_end;
   } else {
     j_lo = s * p.split_keys;
     j_hi = j_lo + p.split_keys < Sk ? j_lo + p.split_keys : Sk;
   }
-  const int r_last = (mb * 16 + 16 < p.rows ? mb * 16 + 16 : p.rows) - 1;
-  const int i_first = (mb * 16) / G;
   if (p.causal) {
     const int lim = r_last / G + Sk - Sq + 1;
     j_hi = lim < j_hi ? lim : j_hi;
   }
   // steps whose keys all lie below this bound need no element mask
-  const int nomask_end = p.causal ? (i_first + Sk - Sq + 1 < Sk ? i_first + Sk - Sq + 1 : Sk) : Sk;
-  const int row_lim = p.causal ? qi + Sk - Sq : 0x7fffffff;
+  int nomask_end = p.causal ? (i_first + Sk - Sq + 1 < Sk ? i_first + Sk - Sq + 1 : Sk) : Sk;
+  int row_lim = p.causal ? qi + Sk - Sq : 0x7fffffff;
+  int row_lo = lp;  // keys below are invisible to this lane's row
+  if constexpr (WIN) {
+    const int64_t diag = (int64_t)qi + Sk - Sq;
+    if (p.wr >= 0) {
+      const int64_t ne = (int64_t)i_first + Sk - Sq + p.wr + 1;
+      nomask_end = ne < nomask_end ? (ne < 0 ? 0 : (int)ne) : nomask_end;
+      const int64_t rl = diag + p.wr;
+      row_lim = rl < row_lim ? (rl < -1 ? -1 : (int)rl) : row_lim;
+    }
+    if (p.wl >= 0) {
+      const int64_t lo = diag - p.wl;
+      row_lo = lo > row_lo ? (int)lo : row_lo;
+    }
+  }
 
   const int64_t q_stride = (int64_t)p.Hq * D;
   const int64_t kv_stride = (int64_t)p.Hkv * D;
   const float c2 = p.scale_log2;
+  // ALiBi slope of this lane's row (its query head) in base-2 units
+  const float slope2 = ALIBI ? p.alibi[(int64_t)b * p.alibi_bstride + qh] * kLog2e : 0.f;
+  const int diag_row = qi + Sk - Sq;
 
   // Q^T fragments: Q[row][32c + 8 g4 .. +7]
   u32x4 qf[D / 32];
@@ -211,13 +260,28 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) sc[kb] = mfma16(kreg[kb][c], qf[c], sc[kb]);
     }
-    if (j0 + TK > nomask_end || (CACHE && j0 < lp)) {
+    if constexpr (LOGIT) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x;
+          if constexpr (CAP) x = softcap2(sc[kb][i], p.cap_k, p.cap2);
+          else x = sc[kb][i] * c2;
+          if constexpr (ALIBI) {
+            const int key = j0 + 8 * g4 + 4 * kb + i;
+            x = __builtin_fmaf(-slope2, __builtin_fabsf((float)(diag_row - key)), x);
+          }
+          sc[kb][i] = x;
+        }
+    }
+    if (j0 + TK > nomask_end || (CACHE && j0 < mask_below)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = j0 + 8 * g4 + 4 * kb + i;
-          if (key >= Sk || key > row_lim || (CACHE && key < lp)) sc[kb][i] = -INFINITY;
+          if (key >= Sk || key > row_lim || (CACHE && key < row_lo)) sc[kb][i] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -227,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
       for (int i = 0; i < 4; ++i) mx = vmax(mx, sc[kb][i]);
     mx = vmax(mx, __shfl_xor(mx, 16));
     mx = vmax(mx, __shfl_xor(mx, 32));
-    const float m_new = vmax(m_run, mx * c2);
+    const float m_new = vmax(m_run, LOGIT ? mx : mx * c2);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
@@ -236,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pe = fast_exp2(__builtin_fmaf(sc[kb][i], c2, -m_use));
+        const float pe = fast_exp2(__builtin_fmaf(sc[kb][i], LOGIT ? 1.f : c2, -m_use));
         sc[kb][i] = pe;
         ls += pe;
       }

@@ -17,11 +17,11 @@ FF_MAX_SPLITS = 128
 FF_SPLIT_BLOCK_N = 128
 STATUS_NAMES = {0: "FF_OK", 1: "FF_ERR_NULL", 2: "FF_ERR_SHAPE", 3: "FF_ERR_HEADDIM",
                 4: "FF_ERR_GQA", 5: "FF_ERR_ALIGN", 6: "FF_ERR_SPLITS", 7: "FF_ERR_SCALE",
-                8: "FF_ERR_HIP", 9: "FF_ERR_ALIAS"}
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_splitkv_num_splits",
+                8: "FF_ERR_HIP", 9: "FF_ERR_ALIAS", 10: "FF_ERR_OPTION"}
+EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_splitkv_num_splits",
            "attn_splits_efficiency_rule", "attn_fwd_splitkv", "attn_splitkv_combine",
-           "attn_fwd_kvcache", "attn_kvcache_append", "attn_bwd_workspace_floats", "attn_bwd",
-           "attn_status_string")
+           "attn_fwd_kvcache", "attn_fwd_kvcache_ex", "attn_kvcache_append",
+           "attn_bwd_workspace_floats", "attn_bwd", "attn_status_string")
 
 
 class FlashFwdError(RuntimeError):
@@ -59,12 +59,14 @@ def load(path=LIB_PATH):
     lib = ctypes.CDLL(os.path.abspath(path))
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+    lib.attn_fwd_ex.argtypes = [P] * 5 + [I] * 9 + [P, I, F, F, P]
     lib.attn_fwd_varlen.argtypes = [P] * 7 + [I] * 8 + [F, P]
     lib.attn_splitkv_num_splits.argtypes = [I, I, I, I, I, I, I]
     lib.attn_splits_efficiency_rule.argtypes = [I, I, I]
     lib.attn_fwd_splitkv.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.attn_splitkv_combine.argtypes = [P, P, P, P, I, I, I, I, I, P]
     lib.attn_fwd_kvcache.argtypes = [P] * 10 + [I] * 10 + [F, I, P]
+    lib.attn_fwd_kvcache_ex.argtypes = [P] * 10 + [I] * 12 + [P, I, F, F, I, P]
     lib.attn_kvcache_append.argtypes = [P] * 6 + [I] * 7 + [P]
     lib.attn_bwd_workspace_floats.argtypes = [I, I, I]
     lib.attn_bwd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, P]
@@ -109,6 +111,14 @@ def attn_status_string(status):
 def attn_fwd(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream=None):
     _check(load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv,
                            d, int(bool(causal)), float(scale), _stream(stream)), "attn_fwd")
+
+
+def attn_fwd_ex(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, window_left, window_right,
+                alibi_slopes, alibi_batch_stride, softcap, scale, stream=None):
+    _check(load().attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv,
+                              d, int(bool(causal)), int(window_left), int(window_right),
+                              _ptr(alibi_slopes), int(alibi_batch_stride), float(softcap),
+                              float(scale), _stream(stream)), "attn_fwd_ex")
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, max_seqlen_q, total_q,
@@ -157,6 +167,19 @@ def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_ta
         float(scale), int(num_splits), _stream(stream)), "attn_fwd_kvcache")
 
 
+def attn_fwd_kvcache_ex(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table,
+                        o_accum, lse_accum, o, lse, B, Sq, Hq, Hkv, d, num_blocks, page_size,
+                        max_blocks_per_seq, new_keys, causal, window_left, window_right,
+                        alibi_slopes, alibi_batch_stride, softcap, scale, num_splits,
+                        stream=None):
+    _check(load().attn_fwd_kvcache_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(cache_leftpad),
+        _ptr(block_table), _ptr(o_accum), _ptr(lse_accum), _ptr(o), _ptr(lse), B, Sq, Hq, Hkv,
+        d, num_blocks, page_size, max_blocks_per_seq, new_keys, int(bool(causal)),
+        int(window_left), int(window_right), _ptr(alibi_slopes), int(alibi_batch_stride),
+        float(softcap), float(scale), int(num_splits), _stream(stream)), "attn_fwd_kvcache_ex")
+
+
 def attn_kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, B, S_new,
                         Hkv, d, num_blocks, page_size, max_blocks_per_seq, stream=None):
     _check(load().attn_kvcache_append(
@@ -182,14 +205,28 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causa
 # ---------------------------------------------------------------------------
 # torch conveniences: allocate outputs with torch, then call the entry points above.
 
-def forward(q, k, v, causal, scale, stream=None):
-    """O [B,Sq,Hq,d] fp32 and LSE [B,Hq,Sq] fp32 from bf16 q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d]."""
+def _alibi_stride(alibi_slopes, Hq):
+    """Batch stride of fp32 slopes [Hq] (0) or [B, Hq] (Hq); None for no slopes."""
+    if alibi_slopes is None:
+        return 0
+    return 0 if alibi_slopes.dim() == 1 else Hq
+
+
+def forward(q, k, v, causal, scale, stream=None, window=(-1, -1), alibi_slopes=None,
+            softcap=0.0):
+    """O [B,Sq,Hq,d] fp32 and LSE [B,Hq,Sq] fp32 from bf16 q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d].
+    window (left, right), fp32 alibi_slopes [Hq] or [B,Hq] and softcap select the mask and
+    bias variants (attn_fwd_ex); without them this is attn_fwd."""
     import torch
     B, Sq, Hq, d = q.shape
     _, Sk, Hkv, _ = k.shape
     o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream)
+    if tuple(window) == (-1, -1) and alibi_slopes is None and not softcap:
+        attn_fwd(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream)
+    else:
+        attn_fwd_ex(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, window[0], window[1],
+                    alibi_slopes, _alibi_stride(alibi_slopes, Hq), softcap, scale, stream)
     return o, lse
 
 
@@ -240,12 +277,14 @@ def _cache_geometry(k_cache, block_table):
 
 
 def forward_kvcache(q, k_cache, v_cache, cache_seqlens, causal, scale, block_table=None,
-                    cache_leftpad=None, new_keys=0, num_splits=0, stream=None):
+                    cache_leftpad=None, new_keys=0, num_splits=0, stream=None, window=(-1, -1),
+                    alibi_slopes=None, softcap=0.0):
     """O [B,Sq,Hq,d] and LSE [B,Hq,Sq] (fp32) of bf16 q [B,Sq,Hq,d] against a key/value
     cache: paged [num_blocks, page, Hkv, d] with int32 block_table [B, max_blocks], or
     contiguous [B, capacity, Hkv, d] without one.  num_splits = 0 takes
     attn_splitkv_num_splits' choice for the capacity; more than one split goes through
-    attn_splitkv_combine."""
+    attn_splitkv_combine.  window, alibi_slopes and softcap as for forward (through
+    attn_fwd_kvcache_ex)."""
     import torch
     B, Sq, Hq, d = q.shape
     num_blocks, page, max_blocks, cap, Hkv, _ = _cache_geometry(k_cache, block_table)
@@ -253,15 +292,19 @@ def forward_kvcache(q, k_cache, v_cache, cache_seqlens, causal, scale, block_tab
         num_splits = attn_splitkv_num_splits(B, Sq, cap, Hq, Hkv, d)
     o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    args = (B, Sq, Hq, Hkv, d, num_blocks, page, max_blocks, new_keys, causal, scale)
+    plain = tuple(window) == (-1, -1) and alibi_slopes is None and not softcap
+    head = (B, Sq, Hq, Hkv, d, num_blocks, page, max_blocks, new_keys, causal)
+    tail = (scale,) if plain else (window[0], window[1], alibi_slopes,
+                                   _alibi_stride(alibi_slopes, Hq), softcap, scale)
+    call = attn_fwd_kvcache if plain else attn_fwd_kvcache_ex
     if num_splits == 1:
-        attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, None,
-                         None, o, lse, *args, 1, stream)
+        call(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, None, None, o, lse,
+             *head, *tail, 1, stream)
         return o, lse
     oa = torch.empty((num_splits, B, Hq, Sq, d), dtype=torch.float32, device=q.device)
     la = torch.empty((num_splits, B, Hq, Sq), dtype=torch.float32, device=q.device)
-    attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, oa, la,
-                     None, None, *args, num_splits, stream)
+    call(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, oa, la, None, None,
+         *head, *tail, num_splits, stream)
     attn_splitkv_combine(oa, la, o, lse, B, Sq, Hq, d, num_splits, stream)
     return o, lse
 

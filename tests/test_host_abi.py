@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         assert ff.status_string(code)
     assert ff.status_string(0) == "ok"
 
@@ -65,6 +65,37 @@ def call_fwd(q=Q, k=K, v=V, o=O, lse=L, **kw):
 ])
 def test_attn_fwd_rejects(kw, code):
     assert call_fwd(**kw) == code
+
+
+AL = 17 << 32   # fake ALiBi slopes
+XGOOD = dict(wl=-1, wr=-1, al=None, ast=0, cap=0.0)
+
+
+def call_fwd_ex(q=Q, k=K, v=V, o=O, lse=L, **kw):
+    a = dict(GOOD, **XGOOD)
+    a.update(kw)
+    return ff.load().attn_fwd_ex(q, k, v, o, lse, a["B"], a["Sq"], a["Sk"], a["Hq"], a["Hkv"],
+                                 a["d"], a["causal"], a["wl"], a["wr"], a["al"], a["ast"],
+                                 a["cap"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    # the plain checks still apply with options set
+    (dict(q=None, wl=4), 1), (dict(B=0, cap=1.0), 2), (dict(d=96, al=AL), 3),
+    (dict(scale=0.0, wr=2), 7), (dict(o=Q, wl=3), 9),
+    # the options themselves
+    (dict(wl=-2), 10), (dict(wr=-5), 10), (dict(cap=-1.0), 10), (dict(cap=float("inf")), 10),
+    (dict(cap=float("nan")), 10), (dict(al=AL, ast=1), 10), (dict(al=AL, ast=3), 10),
+    (dict(al=AL + 2), 5),
+    (dict(al=O, ast=2), 9), (dict(al=L + 4), 9),
+])
+def test_attn_fwd_ex_rejects(kw, code):
+    assert call_fwd_ex(**kw) == code
+
+
+def test_attn_fwd_ex_batch_stride_ignored_without_slopes():
+    # without slopes the stride is not looked at; the call fails on the scale instead
+    assert call_fwd_ex(ast=7, scale=0.0) == 7
 
 
 CQ, CK = 11 << 32, 12 << 32   # fake prefix-sum arrays
@@ -115,6 +146,25 @@ def call_kvcache(q=Q, kc=K, vc=V, sl=SL, lp=LP, bt=BT, oa=None, la=None, o=O, ls
 ])
 def test_attn_fwd_kvcache_rejects(kw, code):
     assert call_kvcache(**kw) == code
+
+
+def call_kvcache_ex(q=Q, kc=K, vc=V, sl=SL, lp=LP, bt=BT, oa=None, la=None, o=O, lse=L, **kw):
+    a = dict(KGOOD, **XGOOD)
+    a.update(kw)
+    return ff.load().attn_fwd_kvcache_ex(q, kc, vc, sl, lp, bt, oa, la, o, lse, a["B"], a["Sq"],
+                                         a["Hq"], a["Hkv"], a["d"], a["nb"], a["page"], a["mb"],
+                                         a["new"], a["causal"], a["wl"], a["wr"], a["al"],
+                                         a["ast"], a["cap"], a["scale"], a["S"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sl=None, wl=2), 1), (dict(S=0, cap=2.0), 6), (dict(page=48, al=AL), 2),
+    (dict(Hq=6, Hkv=4, wr=0), 4), (dict(scale=-1.0, wl=1), 7), (dict(lse=SL, wl=1), 9),
+    (dict(wl=-3), 10), (dict(cap=-0.5), 10), (dict(al=AL, ast=2), 10),
+    (dict(al=AL + 1), 5), (dict(al=O + 16, ast=8), 9),
+])
+def test_attn_fwd_kvcache_ex_rejects(kw, code):
+    assert call_kvcache_ex(**kw) == code
 
 
 def test_kvcache_contiguous_ignores_block_counts():
