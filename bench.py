@@ -42,8 +42,12 @@ HEADLINE = "causal_prefill"
 DECODE = "gqa_decode"
 BACKWARD = "causal_prefill_bwd"   # attn_bwd over causal_prefill's inputs
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_attention_amd", "csrc", f)
-                  for f in ("device.h", "prefill.h", "splitkv.h", "flashfwd.hip")]
+# The device sources each kernel is compiled from (its template code and the shared
+# building blocks); a change to any of them makes its committed counter summary stale.
+KERNEL_SOURCES = {k: [os.path.join(ROOT, "io_aware_attention_amd", "csrc", f) for f in v]
+                  for k, v in {"attn_fwd_prefill": ("device.h", "prefill.h"),
+                               "attn_fwd_splitkv": ("device.h", "splitkv.h"),
+                               "attn_bwd_dkdv": ("device.h", "backward.h")}.items()}
 
 
 def log(*a):
@@ -85,9 +89,9 @@ def decode_bytes(w):
     return kv, q, o, lse
 
 
-def sources_digest():
+def sources_digest(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -105,7 +109,7 @@ def measured_traffic(kernel, workload):
         if "=" in line and not line.lstrip().startswith("#"):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("kernel_sources_sha256") != sources_digest():
+    if kernel not in KERNEL_SOURCES or kv.get("kernel_sources_sha256") != sources_digest(kernel):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
