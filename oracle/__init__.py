@@ -27,6 +27,13 @@ as keywords (the walk-through's Is_local, Has_alibi and Is_softcap):
   window=(left, right)   sliding window around diag = i + Sk - Sq; -1 = no limit
   alibi=slopes           [Hq] or [B, Hq]; -slope * |diag - j| is added to the score
   softcap=c              the scaled score s becomes c * tanh(s / c); 0 = none
+
+FP8 (OCP E4M3; see oracle.c for the format, the block quantizer and the rotation):
+  e4m3_decode(codes) -> float64;  e4m3_encode(x float32) -> uint8 codes
+  fwht(rows float32 [..., d]) -> the rotated rows (float32)
+  quantize_fp8(x, rotate=False) -> (codes uint8 [B,S,H,d], scales float32 [B,H,ceil(S/128)])
+  dequantize_fp8(codes, scales) -> float64 [B,S,H,d]
+  fwd_fp8(q8, k8, v8, qs, ks, vs, causal, scale) -> (o, lse, o_abs, inv_l)
 """
 import ctypes
 import os
@@ -75,6 +82,17 @@ class Oracle:
             ext.restype = ctypes.c_int
         for f in _FWD_FUNCS + ("oracle_attn_bwd",):
             getattr(lib, f).restype = ctypes.c_int
+        L = ctypes.c_int64
+        lib.oracle_e4m3_decode.argtypes = [_P, L, _P]
+        lib.oracle_e4m3_decode.restype = None
+        lib.oracle_e4m3_encode.argtypes = [_P, L, _P]
+        lib.oracle_e4m3_encode.restype = None
+        lib.oracle_fwht_f32.argtypes = [_P, L, _I]
+        lib.oracle_fwht_f32.restype = None
+        lib.oracle_quantize_fp8.argtypes = [_I, _P, _I, _I, _I, _I, _I, _P, _P]
+        lib.oracle_quantize_fp8.restype = ctypes.c_int
+        lib.oracle_attn_fwd_fp8.argtypes = [_P] * 6 + [_I] * 7 + [_D, _P, _P, _P, _P]
+        lib.oracle_attn_fwd_fp8.restype = ctypes.c_int
         self.lib = lib
 
     @staticmethod
@@ -202,6 +220,65 @@ class Oracle:
                                           dv.ctypes.data, dsum.ctypes.data, dq_a.ctypes.data,
                                           dk_a.ctypes.data, dv_a.ctypes.data), "bwd")
         return dq, dk, dv, dsum, (dq_a, dk_a, dv_a)
+
+    # -- FP8 (explainer, FlashAttention-3 precision section)
+
+    def e4m3_decode(self, codes):
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        out = np.empty(c.shape, dtype=np.float64)
+        self.lib.oracle_e4m3_decode(c.ctypes.data, c.size, out.ctypes.data)
+        return out
+
+    def e4m3_encode(self, x):
+        a = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(a.shape, dtype=np.uint8)
+        self.lib.oracle_e4m3_encode(a.ctypes.data, a.size, out.ctypes.data)
+        return out
+
+    def fwht(self, rows):
+        y = np.array(rows, dtype=np.float32, order="C", copy=True)
+        d = y.shape[-1]
+        self.lib.oracle_fwht_f32(y.ctypes.data, y.size // d, d)
+        return y
+
+    def quantize_fp8(self, x, rotate=False):
+        """x: bf16 bits (uint16) or float32 [B,S,H,d]."""
+        a = np.ascontiguousarray(x)
+        if a.dtype == np.uint16:
+            in_bf16 = 1
+        elif a.dtype == np.float32:
+            in_bf16 = 0
+        else:
+            raise TypeError("quantize_fp8 takes bf16 bits (uint16) or float32")
+        B, S, H, d = a.shape
+        codes = np.empty(a.shape, dtype=np.uint8)
+        scales = np.empty((B, H, -(-S // 128)), dtype=np.float32)
+        self._ok(self.lib.oracle_quantize_fp8(in_bf16, a.ctypes.data, B, S, H, d, int(bool(rotate)),
+                                              codes.ctypes.data, scales.ctypes.data),
+                 "quantize_fp8")
+        return codes, scales
+
+    def dequantize_fp8(self, codes, scales):
+        S = codes.shape[1]
+        blk = np.arange(S) // 128
+        sc = np.asarray(scales, dtype=np.float64)[:, :, blk]       # [B, H, S]
+        return self.e4m3_decode(codes) * sc.transpose(0, 2, 1)[..., None]
+
+    def fwd_fp8(self, q8, k8, v8, q_scale, k_scale, v_scale, causal, scale):
+        """The plain definition on the dequantized tensors: (o, lse, o_abs, inv_l)."""
+        arrs = [np.ascontiguousarray(x, dtype=np.uint8) for x in (q8, k8, v8)]
+        scs = [np.ascontiguousarray(x, dtype=np.float32) for x in (q_scale, k_scale, v_scale)]
+        B, Sq, Hq, d = arrs[0].shape
+        _, Sk, Hkv, _ = arrs[1].shape
+        o = np.zeros((B, Sq, Hq, d))
+        lse = np.zeros((B, Hq, Sq))
+        o_abs = np.zeros((B, Sq, Hq, d))
+        inv_l = np.zeros((B, Hq, Sq))
+        self._ok(self.lib.oracle_attn_fwd_fp8(*[x.ctypes.data for x in arrs + scs], B, Sq, Sk,
+                                              Hq, Hkv, d, int(bool(causal)), float(scale),
+                                              o.ctypes.data, lse.ctypes.data, o_abs.ctypes.data,
+                                              inv_l.ctypes.data), "fwd_fp8")
+        return o, lse, o_abs, inv_l
 
     # -- variable-length batches and the paged KV cache ("03 forward CUDA kernel" section 8;
     # "flash attention V2 code walk-through": cu_seqlens as prefix sums, block_table, the

@@ -50,6 +50,18 @@
  *        limit on the logits, the page names no formula; this is its plain form).
  *    The order is: scale, soft cap, ALiBi bias, then the mask.  The soft cap acts
  *    on the dot-product logit alone and the bias is added to the capped logit.
+ *  - FP8 forward (explainer, FlashAttention-3 precision section: FP8 inputs with a
+ *    scale per block, the scales carried into the computation, softmax statistics and
+ *    scaling in fp32, and an orthogonal transform of Q and K that keeps QK^T).  The
+ *    format is OCP FP8 E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *    exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN; no infinities; the
+ *    largest finite value is 448.  A tensor x [B, S, H, d] is quantized per (b, h,
+ *    block of 128 rows): amax = max |x| over the block, scale = fp32(amax / 448) (1 for
+ *    an all-zero block), code = nearest E4M3 value to fp32(x / scale), ties to the even
+ *    code, saturating at +-448.  The optional rotation applies the Walsh-Hadamard
+ *    transform along d (butterflies of distance 1, 2, 4, ..., d/2, each pair (a, b)
+ *    becoming (a + b, a - b) in fp32) and then multiplies by fp32(1 / sqrt(d)).  The FP8
+ *    attention is the plain definition on the dequantized tensors code * scale.
  *  - Backward (explainer, sections "backward: from the softmax derivative",
  *    "training: backward recomputation" and "backward: back to Q, K, V"): with the
  *    dense probability row P of the plain definition and the upstream gradient dO,
@@ -530,4 +542,157 @@ int oracle_attn_bwd(int in_bf16, const void *q, const void *k, const void *v, in
   free(p_all);
   free(ds_all);
   return 0;
+}
+
+/* ---------------------------------------------------------------------------------
+ * FP8 E4M3: decoding, encoding, block quantization, rotation, attention. */
+
+static double e4m3_value(uint8_t c) {
+  const int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+void oracle_e4m3_decode(const uint8_t *codes, int64_t n, double *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(codes[i]);
+}
+
+/* Nearest finite E4M3 value, ties to the even code (its lowest bit 0); beyond 448 the
+ * nearest is 448 (saturation); NaN -> 0x7F.  A search over the 127 non-negative codes. */
+static uint8_t e4m3_encode_one(float x) {
+  if (isnan(x)) return 0x7F;
+  const int neg = signbit(x) != 0;
+  const double a = fabs((double)x);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    const double err = fabs(e4m3_value((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(best | (neg ? 0x80 : 0));
+}
+
+void oracle_e4m3_encode(const float *x, int64_t n, uint8_t *out) {
+  #pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode_one(x[i]);
+}
+
+/* In place, each of nrows rows of d floats: the Walsh-Hadamard butterflies in fp32, then
+ * the fp32 product with fp32(1/sqrt(d)). */
+void oracle_fwht_f32(float *rows, int64_t nrows, int d) {
+  const float inv = (float)(1.0 / sqrt((double)d));
+  for (int64_t r = 0; r < nrows; ++r) {
+    float *y = rows + r * d;
+    for (int h = 1; h < d; h *= 2)
+      for (int i = 0; i < d; ++i)
+        if ((i & h) == 0) {
+          const float a = y[i], b = y[i + h];
+          y[i] = a + b;
+          y[i + h] = a - b;
+        }
+    for (int i = 0; i < d; ++i) y[i] = y[i] * inv;
+  }
+}
+
+/* x [B, S, H, d] (bf16 bits if in_bf16, else floats) -> codes [B, S, H, d] and scales
+ * [B, H, ceil(S / 128)].  rotate: apply oracle_fwht_f32 to every row first.  d must be a
+ * power of two when rotating. */
+int oracle_quantize_fp8(int in_bf16, const void *x, int B, int S, int H, int d, int rotate,
+                        uint8_t *codes, float *scales) {
+  if (!x || !codes || !scales) return 1;
+  if (B < 1 || S < 1 || H < 1 || d < 1) return 2;
+  if (rotate && (d & (d - 1))) return 3;
+  const int nblk = (S + 127) / 128;
+  #pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t u = 0; u < (int64_t)B * H * nblk; ++u) {
+    const int b = (int)(u / ((int64_t)H * nblk)), h = (int)((u / nblk) % H);
+    const int blk = (int)(u % nblk);
+    const int r0 = blk * 128, r1 = r0 + 128 < S ? r0 + 128 : S;
+    float *y = (float *)malloc(sizeof(float) * (size_t)(r1 - r0) * d);
+    for (int r = r0; r < r1; ++r)
+      for (int c = 0; c < d; ++c) {
+        const int64_t idx = (((int64_t)b * S + r) * H + h) * d + c;
+        y[(int64_t)(r - r0) * d + c] =
+            in_bf16 ? (float)elem(x, 1, idx) : ((const float *)x)[idx];
+      }
+    if (rotate) oracle_fwht_f32(y, r1 - r0, d);
+    float amax = 0.f;
+    for (int64_t i = 0; i < (int64_t)(r1 - r0) * d; ++i)
+      if (fabsf(y[i]) > amax) amax = fabsf(y[i]);
+    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+    scales[((int64_t)b * H + h) * nblk + blk] = sc;
+    for (int r = r0; r < r1; ++r)
+      for (int c = 0; c < d; ++c) {
+        const int64_t idx = (((int64_t)b * S + r) * H + h) * d + c;
+        codes[idx] = e4m3_encode_one(y[(int64_t)(r - r0) * d + c] / sc);
+      }
+    free(y);
+  }
+  return 0;
+}
+
+/* Dequantized tensor: code * scale of its (b, h, 128-row block), as doubles. */
+static double *dequantize(const uint8_t *codes, const float *scales, int B, int S, int H,
+                          int d) {
+  const int nblk = (S + 127) / 128;
+  double *out = (double *)malloc(sizeof(double) * (size_t)B * S * H * d);
+  for (int b = 0; b < B; ++b)
+    for (int r = 0; r < S; ++r)
+      for (int h = 0; h < H; ++h)
+        for (int c = 0; c < d; ++c) {
+          const int64_t idx = (((int64_t)b * S + r) * H + h) * d + c;
+          out[idx] = e4m3_value(codes[idx]) * (double)scales[((int64_t)b * H + h) * nblk + r / 128];
+        }
+  return out;
+}
+
+/* The FP8 forward: the plain definition on the dequantized q, k, v.  o, lse as for
+ * oracle_attn_fwd.  If o_abs and inv_l are non-NULL they receive, per row, the sums
+ * o_abs[c] = sum_j P_j |v_jc| ([B, Sq, Hq, d]) and 1 / l with l = sum_j exp(s_j - max s)
+ * ([B, Hq, Sq], 0 for a row without keys), from which the GPU error bound is derived. */
+int oracle_attn_fwd_fp8(const uint8_t *q8, const uint8_t *k8, const uint8_t *v8,
+                        const float *q_scale, const float *k_scale, const float *v_scale,
+                        int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
+                        double scale, double *o, double *lse, double *o_abs, double *inv_l) {
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return 1;
+  if (B < 1 || Sq < 1 || Sk < 1 || Hq < 1 || Hkv < 1 || d < 1) return 2;
+  if (Hq % Hkv) return 3;
+  double *q = dequantize(q8, q_scale, B, Sq, Hq, d);
+  double *k = dequantize(k8, k_scale, B, Sk, Hkv, d);
+  double *v = dequantize(v8, v_scale, B, Sk, Hkv, d);
+  int rc = oracle_attn_fwd(0, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale, o, lse);
+  if (rc == 0 && o_abs && inv_l) {
+    const int in_bf16 = 0;
+    SETUP_PROBLEM
+    (void)err;
+    const int64_t nrows = (int64_t)B * Hq * Sq;
+    #pragma omp parallel
+    {
+      double *srow = (double *)malloc(sizeof(double) * Sk);
+      double *prob = (double *)malloc(sizeof(double) * Sk);
+      #pragma omp for schedule(dynamic, 16)
+      for (int64_t r = 0; r < nrows; ++r) {
+        const int b = (int)(r / ((int64_t)Hq * Sq)), h = (int)((r / Sq) % Hq), i = (int)(r % Sq);
+        double m, l;
+        const int nvis = prob_row(&P, b, h, i, srow, prob, &m, &l);
+        inv_l[((int64_t)b * Hq + h) * Sq + i] = nvis ? 1.0 / l : 0.0;
+        const int hk = kv_head(&P, h);
+        for (int c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int j = 0; j < Sk; ++j) acc += prob[j] * fabs(v[kv_index(&P, b, j, hk, c)]);
+          o_abs[q_index(&P, b, i, h, c)] = acc;
+        }
+      }
+      free(srow);
+      free(prob);
+    }
+  }
+  free(q);
+  free(k);
+  free(v);
+  return rc;
 }

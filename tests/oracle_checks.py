@@ -770,6 +770,157 @@ def check_variants_through_cache_and_varlen(orc):
     assert np.array_equal(o[4:9], ob[0]) and np.array_equal(lse[:, 4:9], lb[0])
 
 
+# ---------------------------------------------------------------------------
+# FP8: the E4M3 format, block quantization, rotation, FP8 attention
+
+
+def check_e4m3_format(orc):
+    g = golden("fp8_e4m3.json")
+    codes = np.arange(256, dtype=np.uint8)
+    val = orc.e4m3_decode(codes)
+    for c, want in g["values"].items():
+        got = val[int(c, 16)]
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (c, got)
+    nan = [int(c, 16) for c in g["nan_codes"]]
+    assert np.isnan(val[nan]).all() and np.isnan(val).sum() == 2
+    pos = val[:0x7F]
+    assert np.all(np.diff(pos) > 0) and pos[-1] == g["max_finite"]
+    assert np.array_equal(val[0x80:0xFF], -pos)
+    assert pos[1] == g["min_subnormal"] and pos[8] == g["min_normal"]
+    # each binade [2^e, 2^(e+1)) of normals holds 8 values spaced 2^(e-3)
+    for e in range(-6, 9):
+        binade = pos[(pos >= 2.0 ** e) & (pos < 2.0 ** (e + 1))]
+        assert len(binade) == (8 if e < 8 else 7), e
+        assert np.allclose(np.diff(binade), 2.0 ** (e - 3), rtol=0, atol=0)
+
+
+def check_e4m3_rounding(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    val = orc.e4m3_decode(codes)
+    fin = ~np.isnan(val)
+    assert np.array_equal(orc.e4m3_encode(val[fin].astype(np.float32)), codes[fin])  # round trip
+    pos = val[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2                 # exactly representable in fp32
+    enc = orc.e4m3_encode(mids.astype(np.float32))
+    lo = np.arange(0, 0x7E)
+    assert np.array_equal(enc, np.where(lo % 2 == 0, lo, lo + 1)), "ties go to the even code"
+    below = np.nextafter(mids.astype(np.float32), np.float32(0))
+    above = np.nextafter(mids.astype(np.float32), np.float32(1e9))
+    assert np.array_equal(orc.e4m3_encode(below), lo) and np.array_equal(orc.e4m3_encode(above), lo + 1)
+    sat = orc.e4m3_encode(np.array([448.0, 463.9, 464.0, 1e6, -1e6], np.float32))
+    assert list(sat) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
+    tiny = orc.e4m3_encode(np.array([2.0 ** -10, 2.0 ** -10 + 2.0 ** -20, -2.0 ** -11, 0.0], np.float32))
+    assert list(tiny) == [0x00, 0x01, 0x80, 0x00]
+    assert orc.e4m3_encode(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def _sylvester(d):
+    h = np.array([[1.0]])
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def check_fwht(orc):
+    rng = np.random.default_rng(1000)
+    for d in (2, 8, 64, 128):
+        x = rng.standard_normal((5, d)).astype(np.float32)
+        y = orc.fwht(x)
+        ref = x.astype(np.float64) @ _sylvester(d) / math.sqrt(d)   # H is symmetric
+        assert np.allclose(y, ref, rtol=0, atol=1e-5 * math.sqrt(d)), d
+        assert np.allclose(orc.fwht(y), x, rtol=0, atol=1e-5 * math.sqrt(d))    # H H / d = I
+        e0 = np.zeros((1, d), np.float32)
+        e0[0, 0] = 1.0
+        assert np.allclose(orc.fwht(e0), 1 / math.sqrt(d), rtol=0, atol=1e-7)
+    # an orthogonal transform of both q and k keeps every dot product
+    q = rng.standard_normal((6, 128)).astype(np.float32)
+    k = rng.standard_normal((9, 128)).astype(np.float32)
+    assert np.allclose(orc.fwht(q).astype(np.float64) @ orc.fwht(k).T.astype(np.float64),
+                       q.astype(np.float64) @ k.T.astype(np.float64), rtol=0, atol=1e-4)
+
+
+def check_quantize_blocks(orc):
+    rng = np.random.default_rng(1001)
+    B, S, H, d = 2, 300, 3, 16
+    x = (rng.standard_normal((B, S, H, d)) * np.exp(rng.uniform(-3, 3, (B, 1, H, 1)))).astype(np.float32)
+    x[1, 128:256, 2] = 0.0                                 # an all-zero block
+    codes, scales = orc.quantize_fp8(x)
+    assert scales.shape == (B, H, 3)
+    val = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+    for b in range(B):
+        for h in range(H):
+            for blk in range(3):
+                rows = slice(128 * blk, min(128 * blk + 128, S))
+                xb = x[b, rows, h]
+                amax = np.abs(xb).max()
+                sc = np.float32(amax) / np.float32(448) if amax > 0 else np.float32(1)
+                assert scales[b, h, blk] == sc, (b, h, blk)
+                cb = codes[b, rows, h]
+                if amax == 0:
+                    assert np.all(cb == 0)
+                    continue
+                # the largest magnitude lands on the top code, and every value is within
+                # half a code spacing of its code (relative 2^-4, absolute 2^-10 near 0)
+                assert (cb & 0x7F).max() == 0x7E
+                y = (xb / sc).astype(np.float64)
+                err = np.abs(val[cb] - y)
+                assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(y), 2.0 ** -10) + 1e-12)
+                assert np.all(np.signbit(val[cb]) == np.signbit(y))
+    # blocks are independent: changing block 1 leaves block 0 and 2 alone
+    x2 = x.copy()
+    x2[0, 130, 0] *= 50.0
+    c2, s2 = orc.quantize_fp8(x2)
+    assert np.array_equal(c2[0, :128], codes[0, :128]) and np.array_equal(c2[0, 256:], codes[0, 256:])
+    assert s2[0, 0, 1] != scales[0, 0, 1] and np.array_equal(s2[0, 0, [0, 2]], scales[0, 0, [0, 2]])
+    # bf16 inputs are widened exactly; rotation is the quantization of the rotated rows
+    bits = synth_bits(rng, (1, 200, 2, 64))
+    cb, sb = orc.quantize_fp8(bits)
+    cf, sf = orc.quantize_fp8(((bits.astype(np.uint32) << 16).view(np.float32)))
+    assert np.array_equal(cb, cf) and np.array_equal(sb, sf)
+    cr, sr = orc.quantize_fp8(bits, rotate=True)
+    rot = orc.fwht((bits.astype(np.uint32) << 16).view(np.float32))
+    c3, s3 = orc.quantize_fp8(rot)
+    assert np.array_equal(cr, c3) and np.array_equal(sr, s3)
+
+
+def synth_bits(rng, shape):
+    """bf16 bit patterns of N(0,1) values (the top half of their float32 bits)."""
+    f = rng.standard_normal(shape).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def check_fp8_attention(orc):
+    rng = np.random.default_rng(1002)
+    for causal, (B, Sq, Sk, Hq, Hkv, d) in ((True, (1, 200, 200, 2, 1, 16)),
+                                           (False, (2, 130, 260, 4, 2, 8))):
+        q = rng.standard_normal((B, Sq, Hq, d)).astype(np.float32)
+        k = rng.standard_normal((B, Sk, Hkv, d)).astype(np.float32)
+        v = rng.standard_normal((B, Sk, Hkv, d)).astype(np.float32)
+        (q8, qs), (k8, ks), (v8, vs) = (orc.quantize_fp8(x) for x in (q, k, v))
+        o, lse, o_abs, inv_l = orc.fwd_fp8(q8, k8, v8, qs, ks, vs, causal, 0.3)
+        # the dequantized tensors, built here from the pinned decode table and the
+        # per-(batch, head, 128-row) scales
+        table = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+
+        def deq(c, sc):
+            blk = np.arange(c.shape[1]) // 128
+            return table[c] * sc[:, :, blk].transpose(0, 2, 1)[..., None].astype(np.float64)
+
+        qd, kd, vd = deq(q8, qs), deq(k8, ks), deq(v8, vs)
+        o2, l2 = orc.fwd(qd, kd, vd, causal, 0.3)
+        assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+        # the dequantized tensors are close to the originals (half a code spacing)
+        assert np.abs(vd - v).max() <= 2.0 ** -4 * np.abs(v).max() + 1e-12
+        g = Hq // Hkv
+        for b, h, i in ((0, 0, 0), (B - 1, Hq - 1, Sq - 1), (0, Hq // 2, Sq // 2)):
+            p = orc.probs(qd, kd, vd, causal, 0.3, b, h, i)
+            assert np.allclose(o_abs[b, i, h], p @ np.abs(vd[b, :, h // g]), rtol=0, atol=TIGHT)
+            s = 0.3 * (kd[b, :, h // g] @ qd[b, i, h])
+            vis = np.arange(Sk) <= i + Sk - Sq if causal else np.ones(Sk, bool)
+            l = np.exp(s[vis] - s[vis].max()).sum()
+            assert abs(inv_l[b, h, i] - 1 / l) < TIGHT
+
+
 ALL_CHECKS = [
     check_online_softmax_example, check_one_query_two_keys, check_exercise_1, check_exercise_2,
     check_causal_mask_pictures, check_tail_tile_case, check_special_cases,
@@ -782,6 +933,7 @@ ALL_CHECKS = [
     check_window_reductions, check_window_printed_range, check_alibi_derived_examples,
     check_alibi_as_extra_feature, check_softcap_closed_forms, check_variants_online_split_agree,
     check_variants_decimal_brute_force, check_variants_through_cache_and_varlen,
+    check_e4m3_format, check_e4m3_rounding, check_fwht, check_quantize_blocks, check_fp8_attention,
 ]
 
 

@@ -33,6 +33,16 @@ MUTANTS = {
                                 "s = tanh(s / p->softcap);"),
     "softcap_before_scale": ("double s = p->scale * acc;\n  if (p->softcap > 0.0) s = p->softcap * tanh(s / p->softcap);",
                              "double s = acc;\n  if (p->softcap > 0.0) s = p->softcap * tanh(s / p->softcap);\n  s *= p->scale;"),
+    # FP8: exponent bias 8, ties away from zero, the scale of the fnuz format (max 240),
+    # 64-row scale blocks when dequantizing, a missing butterfly stage, swapped butterfly
+    "e4m3_bias_8": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "e4m3_ties_away": ("(err == best_err && (c & 1) == 0)", "(err == best_err && 0)"),
+    "fp8_scale_240": ("amax / 448.0f", "amax / 240.0f"),
+    "fp8_dequant_block_64": ("scales[((int64_t)b * H + h) * nblk + r / 128]",
+                             "scales[((int64_t)b * H + h) * nblk + r / 64 % nblk]"),
+    "fwht_missing_stage": ("for (int h = 1; h < d; h *= 2)", "for (int h = 2; h < d; h *= 2)"),
+    "fwht_swapped_pair": ("y[i] = a + b;\n          y[i + h] = a - b;",
+                          "y[i] = a - b;\n          y[i + h] = a + b;"),
 }
 
 
