@@ -37,6 +37,7 @@ import synth  # noqa: E402
 
 METRIC = "attn fwd TFLOP/s (bf16 causal prefill) + decode KV GB/s, % of roofline"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 (E4M3) MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "causal_prefill"
 DECODE = "gqa_decode"
@@ -180,6 +181,56 @@ def run_prefill(torch, ff, name, steps, warmup):
     log(f"[bench] {name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of dense bf16 peak)")
     return res, (q, k, v)
+
+
+def run_fp8(torch, ff, name, steps, warmup):
+    """attn_fwd_fp8 on the workload's tensors quantized by attn_quantize_fp8 (outside the
+    timed region; its own time is reported beside).  Flops as for the bf16 forward."""
+    w = synth.WORKLOADS[name]
+    q, k, v = synth.make_qkv(w)
+    qd, kd, vd = (to_dev(torch, x) for x in (q, k, v))
+    del q, k, v
+    B, Sq, Sk, Hq, Hkv, d = (w[x] for x in ("B", "Sq", "Sk", "Hq", "Hkv", "d"))
+    stream = torch.cuda.current_stream()
+    q8, qs = ff.quantize_fp8(qd, stream=stream)
+    k8, ks = ff.quantize_fp8(kd, stream=stream)
+    v8, vs = ff.quantize_fp8(vd, stream=stream)
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda:0")
+
+    def step():
+        ff.attn_fwd_fp8(q8, k8, v8, qs, ks, vs, o, lse, B, Sq, Sk, Hq, Hkv, d, w["causal"],
+                        w["scale"], stream)
+
+    def quant():
+        ff.attn_quantize_fp8(qd, q8, qs, B, Sq, Hq, d, 0, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    t.start()
+    for _ in range(steps):
+        step()
+    ms = t.stop_ms() / steps
+    t.start()
+    for _ in range(steps):
+        quant()
+    q_ms = t.stop_ms() / steps
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all().item(), f"{name}: non-finite output"
+    flops = prefill_flops(w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    qbytes = B * Sq * Hq * d * 3   # bf16 read, fp8 written
+    log(f"[bench] {name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s "
+        f"({100 * tflops / PEAK_FP8_TFLOPS:.1f}% of dense fp8 peak); quantizing Q takes "
+        f"{q_ms * 1e3:.1f} us ({qbytes / (q_ms * 1e-3) / 1e9:.0f} GB/s)")
+    return {"workload": name, "metric": "TFLOP/s", "value": round(tflops, 2),
+            "ms_per_step": round(ms, 4), "kernel": "attn_fwd_fp8", "dtype": "fp8 e4m3",
+            "algorithmic_flop_per_launch": flops,
+            "quantize_q_ms": round(q_ms, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP8_TFLOPS, 4)}}
 
 
 def run_varlen(torch, ff, name, steps, warmup):
@@ -446,6 +497,8 @@ def main():
             results[name] = run_backward(torch, ff, args.steps, args.warmup)
         elif "total" in synth.WORKLOADS[name]:
             results[name] = run_varlen(torch, ff, name, args.steps, args.warmup)
+        elif synth.WORKLOADS[name].get("fp8"):
+            results[name] = run_fp8(torch, ff, name, args.steps, args.warmup)
         else:
             results[name], inputs = run_prefill(torch, ff, name, args.steps, args.warmup)
             if name == HEADLINE:

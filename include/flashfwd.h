@@ -212,6 +212,32 @@ int attn_kvcache_append(const void* k_new, const void* v_new, void* k_cache, voi
                         int Hkv, int d, int num_blocks, int page_size, int max_blocks_per_seq,
                         void* stream);
 
+/* FP8 quantization ("FlashAttention 1, 2, 3" explainer, FlashAttention-3 precision
+ * section: a scale per block, carried into the computation; Q and K may first go through
+ * a matching orthogonal transform, which keeps QK^T).
+ *   x [B,S,H,d] bf16 -> x_fp8 [B,S,H,d] OCP FP8 E4M3 bytes and scales [B,H,ceil(S/128)]
+ *   fp32: for each (b, h, block of 128 rows) scale = amax / 448 over the block (1 for an
+ *   all-zero block) and code = round-to-nearest-even E4M3 of x / scale (IEEE division).
+ *   rotate != 0 first applies the normalized Walsh-Hadamard transform along d (fp32
+ *   butterflies of distance 1, 2, ..., d/2, then times fp32(1/sqrt(d))); rotate Q and K
+ *   both or neither, never V.
+ * Errors: FF_ERR_NULL, FF_ERR_SHAPE (B, S, H < 1 or 2^31 elements), FF_ERR_HEADDIM,
+ * FF_ERR_ALIGN (16 bytes), FF_ERR_ALIAS (outputs overlapping x or each other). */
+int attn_quantize_fp8(const void* x, void* x_fp8, float* scales, int B, int S, int H, int d,
+                      int rotate, void* stream);
+
+/* FP8 forward: attention on the dequantized tensors code * scale (scales as
+ * attn_quantize_fp8 writes them: q_scale [B,Hq,ceil(Sq/128)], k_scale and v_scale
+ * [B,Hkv,ceil(Sk/128)], positive and finite).  q [B,Sq,Hq,d], k, v [B,Sk,Hkv,d] are E4M3
+ * bytes; o [B,Sq,Hq,d] and lse [B,Hq,Sq] fp32; causal and scale as for attn_fwd.  Both
+ * products run on the fp8 matrix cores with fp32 accumulation; the softmax state is fp32;
+ * the probabilities are rounded to E4M3 for the PV product (the error bound follows from
+ * that rounding, relative 2^-4 per probability).  Errors as for attn_fwd, plus
+ * FF_ERR_NULL for a missing scale array and FF_ERR_ALIAS for outputs overlapping them. */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                 const float* k_scale, const float* v_scale, float* o, float* lse, int B,
+                 int Sq, int Sk, int Hq, int Hkv, int d, int causal, float scale, void* stream);
+
 /* Size of attn_bwd's workspace, in floats: 2 * B * Hq * roundup(Sq, 64).  Returns the
  * count, or the negated ff_status (FF_ERR_SHAPE) for B, Sq or Hq below 1. */
 long long attn_bwd_workspace_floats(int B, int Sq, int Hq);

@@ -14,6 +14,7 @@
 #include "prefill.h"
 #include "splitkv.h"
 #include "backward.h"
+#include "fp8.h"
 
 namespace {
 
@@ -700,6 +701,96 @@ int attn_splitkv_combine(const float* o_accum, const float* lse_accum, float* o,
   const dim3 grid((unsigned)cdiv(rows, 4)), block(256);
   if (d == 128) hipLaunchKernelGGL(ff::attn_splitkv_combine<128>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(ff::attn_splitkv_combine<64>, grid, block, 0, s, p);
+  return launch_status();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int attn_quantize_fp8(const void* x, void* x_fp8, float* scales, int B, int S, int H, int d,
+                      int rotate, void* stream) {
+  if (!x || !x_fp8 || !scales) return FF_ERR_NULL;
+  if (B < 1 || S < 1 || H < 1) return FF_ERR_SHAPE;
+  if (d != 64 && d != 128) return FF_ERR_HEADDIM;
+  const int64_t elems = (int64_t)B * S * H * d;
+  if (elems >= kMaxElems) return FF_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(x_fp8) || !aligned16(scales)) return FF_ERR_ALIGN;
+  const int nblk = (int)cdiv(S, 128);
+  const int64_t sb = (int64_t)B * H * nblk * 4;
+  if (overlaps(x_fp8, elems, x, elems * 2) || overlaps(scales, sb, x, elems * 2) ||
+      overlaps(scales, sb, x_fp8, elems))
+    return FF_ERR_ALIAS;
+  ff::QuantParams p;
+  p.x = (const uint16_t*)x;
+  p.codes = (uint8_t*)x_fp8;
+  p.scales = scales;
+  p.B = B;
+  p.S = S;
+  p.H = H;
+  p.nblk = nblk;
+  p.rotate = rotate ? 1 : 0;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)((int64_t)B * H * nblk)), block(256);
+  if (d == 128) hipLaunchKernelGGL(ff::attn_quantize_fp8<128>, grid, block, 0, s, p);
+  else hipLaunchKernelGGL(ff::attn_quantize_fp8<64>, grid, block, 0, s, p);
+  return launch_status();
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                 const float* k_scale, const float* v_scale, float* o, float* lse, int B,
+                 int Sq, int Sk, int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !q_scale || !k_scale || !v_scale || !o || !lse) return FF_ERR_NULL;
+  int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
+  if (st) return st;
+  const void* ptrs[8] = {q, k, v, q_scale, k_scale, v_scale, o, lse};
+  for (const void* x : ptrs)
+    if (!aligned16(x)) return FF_ERR_ALIGN;
+  if ((st = check_scale(scale))) return st;
+  const int nqb = (int)cdiv(Sq, 128), nkb = (int)cdiv(Sk, 128);
+  const int64_t qb = (int64_t)B * Sq * Hq * d, kvb = (int64_t)B * Sk * Hkv * d;
+  const void* ins[6] = {q, k, v, q_scale, k_scale, v_scale};
+  const int64_t in_b[6] = {qb, kvb, kvb, (int64_t)B * Hq * nqb * 4, (int64_t)B * Hkv * nkb * 4,
+                           (int64_t)B * Hkv * nkb * 4};
+  const void* outs[2] = {o, lse};
+  const int64_t ob[2] = {qb * 4, (int64_t)B * Hq * Sq * 4};
+  if (overlaps(o, ob[0], lse, ob[1])) return FF_ERR_ALIAS;
+  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], ob[i], ins[j], in_b[j])) return FF_ERR_ALIAS;
+
+  ff::Fp8Params p;
+  p.q = (const uint8_t*)q;
+  p.k = (const uint8_t*)k;
+  p.v = (const uint8_t*)v;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.num_m = (int)cdiv(Sq, ff::Fp8Traits<128>::BM);
+  p.u_per = (int)cdiv((int64_t)B * Hkv, 8);
+  const int64_t total = 8 * (int64_t)p.u_per * p.G * p.num_m;
+  if (total >= kMaxElems) return FF_ERR_SHAPE;
+  p.total = (int)total;
+  p.nqb = nqb;
+  p.nkb = nkb;
+  p.scale_log2 = scale * ff::kLog2e;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)total), block(256);
+  if (d == 128) {
+    if (causal) hipLaunchKernelGGL((ff::attn_fwd_fp8<128, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ff::attn_fwd_fp8<128, false>), grid, block, 0, s, p);
+  } else {
+    if (causal) hipLaunchKernelGGL((ff::attn_fwd_fp8<64, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((ff::attn_fwd_fp8<64, false>), grid, block, 0, s, p);
+  }
   return launch_status();
 }
 

@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "FF_OK", 1: "FF_ERR_NULL", 2: "FF_ERR_SHAPE", 3: "FF_ERR_HEAD
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_splitkv_num_splits",
            "attn_splits_efficiency_rule", "attn_fwd_splitkv", "attn_splitkv_combine",
            "attn_fwd_kvcache", "attn_fwd_kvcache_ex", "attn_kvcache_append",
-           "attn_bwd_workspace_floats", "attn_bwd", "attn_status_string")
+           "attn_quantize_fp8", "attn_fwd_fp8", "attn_bwd_workspace_floats", "attn_bwd",
+           "attn_status_string")
 
 
 class FlashFwdError(RuntimeError):
@@ -68,6 +69,8 @@ def load(path=LIB_PATH):
     lib.attn_fwd_kvcache.argtypes = [P] * 10 + [I] * 10 + [F, I, P]
     lib.attn_fwd_kvcache_ex.argtypes = [P] * 10 + [I] * 12 + [P, I, F, F, I, P]
     lib.attn_kvcache_append.argtypes = [P] * 6 + [I] * 7 + [P]
+    lib.attn_quantize_fp8.argtypes = [P, P, P, I, I, I, I, I, P]
+    lib.attn_fwd_fp8.argtypes = [P] * 8 + [I] * 7 + [F, P]
     lib.attn_bwd_workspace_floats.argtypes = [I, I, I]
     lib.attn_bwd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, P]
     lib.attn_status_string.argtypes = [I]
@@ -186,6 +189,18 @@ def attn_kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_tab
         _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
         _ptr(block_table), B, S_new, Hkv, d, num_blocks, page_size, max_blocks_per_seq,
         _stream(stream)), "attn_kvcache_append")
+
+
+def attn_quantize_fp8(x, x_fp8, scales, B, S, H, d, rotate, stream=None):
+    _check(load().attn_quantize_fp8(_ptr(x), _ptr(x_fp8), _ptr(scales), B, S, H, d,
+                                    int(bool(rotate)), _stream(stream)), "attn_quantize_fp8")
+
+
+def attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Sq, Sk, Hq, Hkv, d, causal,
+                 scale, stream=None):
+    _check(load().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                               _ptr(v_scale), _ptr(o), _ptr(lse), B, Sq, Sk, Hq, Hkv, d,
+                               int(bool(causal)), float(scale), _stream(stream)), "attn_fwd_fp8")
 
 
 def attn_bwd_workspace_floats(B, Sq, Hq):
@@ -316,6 +331,30 @@ def kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_table=No
     num_blocks, page, max_blocks, _, _, _ = _cache_geometry(k_cache, block_table)
     attn_kvcache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, block_table, B, S_new,
                         Hkv, d, num_blocks, page, max_blocks, stream)
+
+
+def quantize_fp8(x, rotate=False, stream=None):
+    """E4M3 codes (torch.uint8, x's shape) and fp32 block scales [B,H,ceil(S/128)] of a bf16
+    tensor x [B,S,H,d]; rotate applies the Walsh-Hadamard transform along d first."""
+    import torch
+    B, S, H, d = x.shape
+    codes = torch.empty((B, S, H, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, H, -(-S // 128)), dtype=torch.float32, device=x.device)
+    attn_quantize_fp8(x, codes, scales, B, S, H, d, rotate, stream)
+    return codes, scales
+
+
+def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal, scale, stream=None):
+    """O [B,Sq,Hq,d] and LSE [B,Hq,Sq] (fp32) from E4M3 q8 [B,Sq,Hq,d], k8/v8 [B,Sk,Hkv,d]
+    and their block scales."""
+    import torch
+    B, Sq, Hq, d = q8.shape
+    _, Sk, Hkv, _ = k8.shape
+    o = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device=q8.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, Sq, Sk, Hq, Hkv, d, causal,
+                 scale, stream)
+    return o, lse
 
 
 def backward(q, k, v, o, lse, dout, causal, scale, stream=None):

@@ -167,6 +167,41 @@ def test_attn_fwd_kvcache_ex_rejects(kw, code):
     assert call_kvcache_ex(**kw) == code
 
 
+QS, KS, VS = 18 << 32, 19 << 32, 20 << 32   # fake scale arrays
+
+
+def call_fwd_fp8(q=Q, k=K, v=V, qs=QS, ks=KS, vs=VS, o=O, lse=L, **kw):
+    a = dict(GOOD, **kw)
+    return ff.load().attn_fwd_fp8(q, k, v, qs, ks, vs, o, lse, a["B"], a["Sq"], a["Sk"], a["Hq"],
+                                  a["Hkv"], a["d"], a["causal"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=None), 1), (dict(vs=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(Sk=0), 2), (dict(d=96), 3), (dict(Hq=3, Hkv=2), 4),
+    (dict(ks=KS + 4), 5), (dict(q=Q + 8), 5),
+    (dict(scale=0.0), 7),
+    (dict(o=QS - 16), 9), (dict(lse=VS), 9), (dict(o=K), 9),
+])
+def test_attn_fwd_fp8_rejects(kw, code):
+    assert call_fwd_fp8(**kw) == code
+
+
+def call_quantize(x=Q, x8=K, sc=QS, **kw):
+    a = dict(dict(B=2, S=300, H=3, d=128, rotate=0), **kw)
+    return ff.load().attn_quantize_fp8(x, x8, sc, a["B"], a["S"], a["H"], a["d"], a["rotate"],
+                                       None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(sc=None), 1), (dict(B=0), 2), (dict(S=0), 2),
+    (dict(S=1 << 24, H=1 << 4), 2), (dict(d=32), 3), (dict(x8=K + 4), 5),
+    (dict(x8=Q + 512), 9), (dict(sc=Q + 64), 9), (dict(sc=K + 64), 9),
+])
+def test_attn_quantize_fp8_rejects(kw, code):
+    assert call_quantize(**kw) == code
+
+
 def test_kvcache_contiguous_ignores_block_counts():
     # without a block table the caches are [B, page_size, Hkv, d]: page_size need not be a
     # multiple of 32, and num_blocks / max_blocks_per_seq are not looked at (the call
