@@ -106,6 +106,9 @@ WORKLOADS = {
     # causal_prefill's tensors, quantized to FP8 E4M3 with 128-row block scales
     "causal_prefill_fp8": dict(B=4, Sq=4096, Sk=4096, Hq=16, Hkv=16, d=128, causal=True,
                                scale=f32(1 / np.sqrt(128.0)), seed=2, mult=1.0, fp8=True),
+    # long_causal_gqa's tensors in FP8
+    "long_causal_gqa_fp8": dict(B=1, Sq=16384, Sk=16384, Hq=32, Hkv=8, d=128, causal=True,
+                                scale=f32(1 / np.sqrt(128.0)), seed=5, mult=0.5, fp8=True),
     # causal_prefill's 16384 tokens as a packed batch of sequences of mixed length
     # (seq_lengths: uniform on [1, 4096]); q/k/v [16384, H, d], cu_seqlens prefix sums
     "varlen_prefill": dict(total=16384, max_len=4096, Hq=16, Hkv=16, d=128, causal=True,
