@@ -145,7 +145,7 @@ __device__ __forceinline__ constexpr int perm_row(int e) {
 // ---------------------------------------------------------------------------
 // attn_bwd_dq: one workgroup per (128-query tile, batch, query head).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist for the device target only
   constexpr int BM = 128, BN = 64;
   using T = BwdTraits<D, BN>;
@@ -240,45 +240,37 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq(BwdParams p) {
     if (t + 1 < n_max) issue(t + 1);  // into the other buffers, free since the last barrier
     const uint32_t kl = smem_addr + (t & 1) * TILE;
     const uint32_t vl = smem_addr + (2 + (t & 1)) * TILE;
-    // S^T (keys x queries) = K Q^T and dP^T = V dO^T, two 32-key blocks
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        s[kb] = mfma32(lds_b128(kl + ad.row[c] + kb * 32 * ROWB), qf[c], s[kb]);
-        dp[kb] = mfma32(lds_b128(vl + ad.row[c] + kb * 32 * ROWB), of[c], dp[kb]);
-      }
-    }
-    // dS^T = P^T (dP^T - D) with P^T = 2^(s c2 - L2); masked keys give 0
+    // per 32-key block kb: S^T = K Q^T and dP^T = V dO^T, dS^T = P^T (dP^T - D) with
+    // P^T = 2^(s c2 - L2) (masked keys give 0), then dQ^T += K^T dS^T through transposing
+    // reads of the K tile
     const bool masked = t >= n_mask;
     const int vis = last_key - t * BN - 8 * H;  // key offsets <= vis are visible
-    u32x4 dsf[2][2];
+    static_for<2>([&](auto KB) {
+      constexpr int kb = decltype(KB)::value;
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int c = 0; c < D / 16; ++c) {
+        s = mfma32(lds_b128(kl + ad.row[c] + kb * 32 * ROWB), qf[c], s);
+        dp = mfma32(lds_b128(vl + ad.row[c] + kb * 32 * ROWB), of[c], dp);
+      }
       float ds[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        float pr = fast_exp2(__builtin_fmaf(s[kb][e], c2, -L2));
+        float pr = fast_exp2(__builtin_fmaf(s[e], c2, -L2));
         if (masked && 32 * kb + perm_row(e) > vis) pr = 0.f;
-        ds[e] = pr * (dp[kb][e] - Dr);
+        ds[e] = pr * (dp[e] - Dr);
       }
+      u32x4 dsf[2];
 #pragma unroll
       for (int cp = 0; cp < 2; ++cp)
-        dsf[kb][cp] = pack8(ds[8 * cp], ds[8 * cp + 1], ds[8 * cp + 2], ds[8 * cp + 3],
-                            ds[8 * cp + 4], ds[8 * cp + 5], ds[8 * cp + 6], ds[8 * cp + 7]);
-    }
-    // dQ^T (dcols x queries) += K^T dS^T; K^T through transposing reads of the K tile
-    static_for<2>([&](auto KB) {
-      constexpr int kb = decltype(KB)::value;
+        dsf[cp] = pack8(ds[8 * cp], ds[8 * cp + 1], ds[8 * cp + 2], ds[8 * cp + 3],
+                        ds[8 * cp + 4], ds[8 * cp + 5], ds[8 * cp + 6], ds[8 * cp + 7]);
       static_for<2>([&](auto CP) {
         constexpr int cp = decltype(CP)::value;
         constexpr int off = (32 * kb + 16 * cp) * ROWB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          dqacc[db] = mfma32(tr_operand<off>(kl, ad.tlo[db], ad.thi[db]), dsf[kb][cp], dqacc[db]);
+          dqacc[db] = mfma32(tr_operand<off>(kl, ad.tlo[db], ad.thi[db]), dsf[cp], dqacc[db]);
       });
     });
     wait_vmem();
