@@ -80,7 +80,18 @@ struct BwdTraits {
   static constexpr int TILE = TROWS * ROWB;               // bytes per streamed tile
   static constexpr int RPB = 256 / ROWB;                  // rows per 256-byte line
   static constexpr int LOADS = TROWS * CPR / kThreads;    // 16-byte loads per thread per tile
-  static __device__ __forceinline__ int swz(int r) { return (r / RPB) % CPR; }
+  // LDS banks span 256-byte lines.  The 128-bit row reads take 16 lanes (16 rows, one
+  // logical chunk) at a time and the transposing reads 32 lanes (4 rows x 4 chunks of
+  // an aligned group of four) at a time, so the XOR key must be one-to-one over the
+  // lines of 16 rows and must differ in bits 2 and up across 4 consecutive rows: the
+  // key of line u swaps the 2-bit fields of u (one bit of u at d = 64, where a line
+  // holds two rows and the key has three bits).
+  static __device__ __forceinline__ int swz(int r) {
+    constexpr int L = 4 / RPB;  // lines per 4 rows
+    const int u = r / RPB;
+    return ((u % L) << 2) | ((u / L) % 4);
+  }
+  static_assert(D == 64 || D == 128, "head dimension");
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -293,21 +304,36 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// attn_bwd_dkdv: one workgroup per (128 keys, batch, key/value head); its query
-// tiles are those of every query head of the group.
+// attn_bwd_dkdv: one workgroup of 8 wavefronts per (128 keys, batch, key/value head);
+// its query tiles (64 rows) are those of every query head of the group.  Each tile goes
+// through two phases:
+//   1. wavefront w takes query block qb = w / 4 and key block kb = w % 4 (32 x 32):
+//      S = Q K^T, dP = dO V^T (K and V fragments of the block resident), P and
+//      dS = P (dP - D); P and dS go to LDS as bf16, [key][query];
+//   2. wavefront w takes key block kb = w % 4 and half dh = w / 4 of the head
+//      dimension: dV^T += dO^T P and dK^T += Q^T dS over the tile's 64 queries, dO^T
+//      and Q^T through transposing reads, P and dS read back from LDS.
+// Splitting the accumulators over two wavefronts keeps each at 32 keys x d/2, so two
+// wavefronts fit on a SIMD.  Each tile costs two workgroup barriers: the one at its
+// start also orders the previous tile's phase 2 before this tile's phase 1, so P and
+// dS need one buffer each.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int BK = 128, BQ = 64;
+  constexpr int BK = 128, BQ = 64, NT = 512;
+  constexpr int ROWB = D * 2, CPR = D / 8, TILE = BQ * ROWB;
+  constexpr int LOADS = BQ * CPR / NT;          // 16-byte loads per thread per tile
+  constexpr int PROWB = BQ * 2;                 // bytes per key row of the P / dS buffers
+  constexpr int PBUF = BK * PROWB;              // the P or the dS buffer
+  constexpr int DH = D / 64;                    // 32-dcol blocks per half of d
   using T = BwdTraits<D, BQ>;
-  constexpr int ROWB = T::ROWB, CPR = T::CPR, TILE = T::TILE, LOADS = T::LOADS;
-  // Q tiles 0/1, dO tiles 2/3, then L2 and D slots (1 KiB each: the 64 values use the
-  // first 256 bytes, the rest of the load lands as zeros)
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 4 * 1024];
+  // Q tiles 0/1, dO tiles 2/3, P, dS, then L2 and D slots 0/1 (1 KiB each: the 64
+  // values use the first 256 bytes, the rest of the load lands as zeros)
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 2 * PBUF + 4 * 1024];
 
   const int total = p.num_n * p.B * p.Hkv;
   const int idx = xcd_remap(blockIdx.x, total);
-  const int unit = idx / p.num_n, nb = idx - unit * p.num_n;  // low key blocks: most queries
+  const int unit = idx / p.num_n, nb = idx - unit * p.num_n;
   const int b = unit / p.Hkv, hk = unit % p.Hkv;
   const int k0 = nb * BK;
   const int Sq = p.Sq, Sk = p.Sk;
@@ -316,15 +342,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int n = lane & 31, H = lane >> 5;
-  const int key = k0 + wave * 32 + n;
+  const int kb = wave & 3;       // key block of both phases
+  const int qb = wave >> 2;      // phase 1: query block
+  const int dh = wave >> 2;      // phase 2: half of the head dimension
+  const int key = k0 + 32 * kb + n;
 
-  // query tiles [qt_lo, num_qt) of each head; tiles below qt_mask need no mask
+  // query tiles [qt_lo, num_qt) of each head; tiles below qt_mask need a mask
   const int num_qt = (Sq + BQ - 1) / BQ;
   int qt_lo = 0, qt_mask = 0;
   if (CAUSAL) {
     const int first_q = k0 - (Sk - Sq);  // first query that sees key k0
     qt_lo = first_q <= 0 ? 0 : (first_q / BQ < num_qt ? first_q / BQ : num_qt);
-    // a tile needs a mask iff some key of the block lies past its first query's limit
     const int q_full = k0 + BK - 1 - (Sk - Sq);  // queries >= q_full see every key of the block
     qt_mask = q_full <= 0 ? 0 : (q_full + BQ - 1) / BQ;
   }
@@ -333,10 +361,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(BwdParams p) {
 
   const int64_t kv_stride = (int64_t)p.Hkv * D;
   const int q_row_bytes = p.Hq * D * 2;
-  float* dk_row = p.dk + ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D;
-  float* dv_row = p.dv + ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D;
 
-  // resident K and V fragments (B operands of S = Q K^T and dP = dO V^T)
+  // resident K and V fragments of key block kb (B operands of S = Q K^T, dP = dO V^T)
   u32x4 kf[D / 16], vf[D / 16];
   {
     const int64_t off = ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D + 8 * H;
@@ -348,9 +374,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   }
 
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  f32x16 dkacc[DH], dvacc[DH];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
+  for (int i = 0; i < DH; ++i) {
     dkacc[i] = f32x16{};
     dvacc[i] = f32x16{};
   }
@@ -364,6 +390,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(BwdParams p) {
       loff[j] = r * q_row_bytes + 16 * (ph ^ T::swz(r));
     }
     const uint32_t smem_addr = lds_addr(smem);
+    const uint32_t s_base = smem_addr + 4 * TILE + 2 * PBUF;  // L2 0/1, then D 0/1
     // item it: head h = hk*G + it / per_head, query tile qt_lo + it % per_head
     auto issue = [&](int it) {
       const int h = hk * p.G + it / per_head;
@@ -379,95 +406,140 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv(BwdParams p) {
         const float* src = (wave == 0 ? p.lse2 : p.dsum) + ((int64_t)b * p.Hq + h) * p.sq_pad + q0;
         const int nv = rows < BQ ? rows : BQ;
         const i32x4 rd = buffer_desc(src, (uint32_t)nv * 4u);
-        const uint32_t dst = smem_addr + 4 * TILE + (2 * wave + par) * 1024;
+        const uint32_t dst = s_base + (2 * wave + par) * 1024;
         buffer_load_lds16(rd, 16 * lane, __builtin_amdgcn_readfirstlane(dst));
       }
     };
+    // Per-lane LDS offsets, fixed for the whole loop; the tile parity is a compile-time
+    // constant in each copy of the loop body, so every LDS access is one of these plus an
+    // immediate.
     const BwdAddr<D, BQ> ad(lane);
+    int arow[D / 16];  // phase 1 A operand: row read of query block qb, chunk 2c + H
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) arow[c] = ad.row[c] + qb * 32 * ROWB;
+    // transposing-read offsets of this wavefront's dcol blocks dh*DH + j (the layout of
+    // BwdAddr::tlo / thi)
+    int tlo[DH], thi[DH];
+    {
+      const int g = lane >> 4, s = lane & 15;
+      const int vrow = 8 * (g >> 1) + (s >> 2);
+#pragma unroll
+      for (int j = 0; j < DH; ++j) {
+        const int chunk = 4 * (dh * DH + j) + 2 * (g & 1) + ((s & 3) >> 1);
+        tlo[j] = vrow * ROWB + 16 * (chunk ^ T::swz(vrow)) + 8 * (s & 1);
+        thi[j] = (vrow + 4) * ROWB + 16 * (chunk ^ T::swz(vrow + 4)) + 8 * (s & 1);
+      }
+    }
+    // P / dS buffers: row = key in the block (128 bytes: 64 queries, two rows per
+    // 256-byte bank line), 16-byte chunk c of row r stored at chunk c ^ ((r / 2) % 8), so
+    // the 16 rows a 128-bit access serves at once hit distinct banks
+    auto pchunk = [](int r, int c) { return r * PROWB + 16 * (c ^ ((r >> 1) & 7)); };
+    const int prow = 32 * kb + n;
+    int pwr[2], prd[4];  // phase 1 writes (queries 32qb + 16half + 8H ..), phase 2 reads
+#pragma unroll
+    for (int half = 0; half < 2; ++half) pwr[half] = pchunk(prow, 4 * qb + H + 2 * half);
+#pragma unroll
+    for (int cq = 0; cq < 4; ++cq) prd[cq] = pchunk(prow, 2 * cq + H);
+    const int srow = 4 * (32 * qb + 8 * H);  // L2 / D of queries 32qb + 8H ..
     const float c2 = p.scale_log2;
+    const uint32_t lds0 = lds_addr(smem);
+    constexpr uint32_t P_OFF = 4 * TILE, DS_OFF = 4 * TILE + PBUF, S_OFF = 4 * TILE + 2 * PBUF;
+    auto st_lds = [](uint32_t a, u32x4 v) {
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>((uintptr_t)a) = v;
+    };
+
+    // one tile: PAR is the parity of item it (LDS buffers of its Q, dO, L2 and D)
+    auto step = [&](auto PARC, int it) {
+      constexpr uint32_t PAR = decltype(PARC)::value;
+      constexpr uint32_t Q_OFF = PAR * TILE, O_OFF = (2 + PAR) * TILE;
+      constexpr uint32_t L2_OFF = S_OFF + PAR * 1024, DD_OFF = S_OFF + (2 + PAR) * 1024;
+      wait_vmem();
+      __syncthreads();  // tile it in LDS; phase 2 of tile it-1 done everywhere
+      if (it + 1 < items) issue(it + 1);
+      const int qt = qt_lo + it % per_head;
+      const bool masked = CAUSAL && qt < qt_mask;
+
+      // ---- phase 1: S, dP of (qb, kb); P, dS -> LDS.  Lane (key n, H) holds queries
+      // 32 qb + 8H + {0..7} (elements 0..7) and + 16 (elements 8..15).
+      f32x16 sacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) sacc = mfma32(lds_b128(lds0 + Q_OFF + arow[c]), kf[c], sacc);
+      float pr[16];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {  // elements 4w .. 4w+3: queries 16(w/2) + 4(w%2) + ..
+        const u32x4 l2 = lds_b128(lds0 + L2_OFF + srow + 4 * (16 * (w >> 1) + 4 * (w & 1)));
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          pr[4 * w + x] = fast_exp2(__builtin_fmaf(sacc[4 * w + x], c2, -__uint_as_float(l2[x])));
+      }
+      if (masked) {
+        // key <= q + Sk - Sq  <=>  query offset in the tile >= key - (Sk - Sq) - q0
+        const int need = key - (Sk - Sq) - qt * BQ - 8 * H - 32 * qb;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (perm_row(e) < need) pr[e] = 0.f;
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        st_lds(lds0 + P_OFF + pwr[half],
+               pack8(pr[8 * half], pr[8 * half + 1], pr[8 * half + 2], pr[8 * half + 3],
+                     pr[8 * half + 4], pr[8 * half + 5], pr[8 * half + 6], pr[8 * half + 7]));
+      f32x16 dpacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) dpacc = mfma32(lds_b128(lds0 + O_OFF + arow[c]), vf[c], dpacc);
+      float ds[16];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const u32x4 dd = lds_b128(lds0 + DD_OFF + srow + 4 * (16 * (w >> 1) + 4 * (w & 1)));
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          ds[4 * w + x] = pr[4 * w + x] * (dpacc[4 * w + x] - __uint_as_float(dd[x]));
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        st_lds(lds0 + DS_OFF + pwr[half],
+               pack8(ds[8 * half], ds[8 * half + 1], ds[8 * half + 2], ds[8 * half + 3],
+                     ds[8 * half + 4], ds[8 * half + 5], ds[8 * half + 6], ds[8 * half + 7]));
+      __syncthreads();  // P and dS of the whole tile written
+
+      // ---- phase 2: dV^T += dO^T P, dK^T += Q^T dS for key block kb, dcols of half dh,
+      // over the tile's four 16-query chunks
+      static_for<4>([&](auto CQ) {
+        constexpr int cq = decltype(CQ)::value;
+        constexpr int rowoff = 16 * cq * ROWB;
+        const u32x4 pb = lds_b128(lds0 + P_OFF + prd[cq]);
+        const u32x4 sb = lds_b128(lds0 + DS_OFF + prd[cq]);
+#pragma unroll
+        for (int j = 0; j < DH; ++j) {
+          dvacc[j] = mfma32(tr_operand<rowoff>(lds0 + O_OFF, tlo[j], thi[j]), pb, dvacc[j]);
+          dkacc[j] = mfma32(tr_operand<rowoff>(lds0 + Q_OFF, tlo[j], thi[j]), sb, dkacc[j]);
+        }
+      });
+    };
 
     issue(0);
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < items; ++it) {
-      if (it + 1 < items) issue(it + 1);
-      const uint32_t par = it & 1;
-      const uint32_t ql = smem_addr + par * TILE;
-      const uint32_t ol = smem_addr + (2 + par) * TILE;
-      const uint32_t l2l = smem_addr + 4 * TILE + par * 1024;
-      const uint32_t dsl = smem_addr + 4 * TILE + (2 + par) * 1024;
-      const int qt = qt_lo + it % per_head;
-      const int q0 = qt * BQ;
-      const bool masked = CAUSAL && qt < qt_mask;
-      // key <= q + Sk - Sq  <=>  query offset in the tile >= key - (Sk - Sq) - q0
-      const int need = key - (Sk - Sq) - q0 - 8 * H;  // row offsets below need are masked
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // S (queries x keys) = Q K^T and dP = dO V^T for 32 queries
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          s = mfma32(lds_b128(ql + ad.row[c] + qb * 32 * ROWB), kf[c], s);
-          dp = mfma32(lds_b128(ol + ad.row[c] + qb * 32 * ROWB), vf[c], dp);
-        }
-        // L2 and D of this lane's 16 query rows: rows 32qb + 8H + {0..7} and +16
-        float l2[16], dd[16];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            const uint32_t o = 4 * (32 * qb + 16 * half + 8 * H + 4 * w);
-            const u32x4 a = lds_b128(l2l + o), c = lds_b128(dsl + o);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              l2[8 * half + 4 * w + x] = __uint_as_float(a[x]);
-              dd[8 * half + 4 * w + x] = __uint_as_float(c[x]);
-            }
-          }
-        u32x4 pf[2], dsf[2];
-        float pr[16], ds[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = fast_exp2(__builtin_fmaf(s[e], c2, -l2[e]));
-          if (masked && 32 * qb + perm_row(e) < need) x = 0.f;
-          pr[e] = x;
-          ds[e] = x * (dp[e] - dd[e]);
-        }
-#pragma unroll
-        for (int cp = 0; cp < 2; ++cp) {
-          pf[cp] = pack8(pr[8 * cp], pr[8 * cp + 1], pr[8 * cp + 2], pr[8 * cp + 3],
-                         pr[8 * cp + 4], pr[8 * cp + 5], pr[8 * cp + 6], pr[8 * cp + 7]);
-          dsf[cp] = pack8(ds[8 * cp], ds[8 * cp + 1], ds[8 * cp + 2], ds[8 * cp + 3],
-                          ds[8 * cp + 4], ds[8 * cp + 5], ds[8 * cp + 6], ds[8 * cp + 7]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS through transposing reads
-        static_for<2>([&](auto CP) {
-          constexpr int cp = decltype(CP)::value;
-          const uint32_t rowoff = (32 * qb + 16 * cp) * ROWB;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            dvacc[db] = mfma32(tr_operand<0>(ol + rowoff, ad.tlo[db], ad.thi[db]), pf[cp], dvacc[db]);
-            dkacc[db] = mfma32(tr_operand<0>(ql + rowoff, ad.tlo[db], ad.thi[db]), dsf[cp], dkacc[db]);
-          }
-        });
-      }
-      wait_vmem();
-      __syncthreads();
+    int it = 0;
+    for (; it + 1 < items; it += 2) {
+      step(std::integral_constant<uint32_t, 0>{}, it);
+      step(std::integral_constant<uint32_t, 1>{}, it + 1);
     }
+    if (it < items) step(std::integral_constant<uint32_t, 0>{}, it);
   }
 
   // dK = scale * dK^T, dV = dV^T: element 4j + i of block db is dcol 32db + 8j + 4H + i
   if (key < Sk) {
+    float* dk_row = p.dk + ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D;
+    float* dv_row = p.dv + ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D;
     const float sc = p.scale;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int jb = 0; jb < DH; ++jb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int c = 32 * db + 8 * j + 4 * H;
-        st16f(dk_row + c, f32x4{dkacc[db][4 * j] * sc, dkacc[db][4 * j + 1] * sc,
-                                dkacc[db][4 * j + 2] * sc, dkacc[db][4 * j + 3] * sc});
-        st16f(dv_row + c, f32x4{dvacc[db][4 * j], dvacc[db][4 * j + 1], dvacc[db][4 * j + 2],
-                                dvacc[db][4 * j + 3]});
+        const int c = 32 * (dh * DH + jb) + 8 * j + 4 * H;
+        st16f(dk_row + c, f32x4{dkacc[jb][4 * j] * sc, dkacc[jb][4 * j + 1] * sc,
+                                dkacc[jb][4 * j + 2] * sc, dkacc[jb][4 * j + 3] * sc});
+        st16f(dv_row + c, f32x4{dvacc[jb][4 * j], dvacc[jb][4 * j + 1], dvacc[jb][4 * j + 2],
+                                dvacc[jb][4 * j + 3]});
       }
   }
 #endif

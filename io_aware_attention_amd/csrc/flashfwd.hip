@@ -233,23 +233,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
   const dim3 block(256);
   const dim3 g_prep((unsigned)cdiv((int64_t)B * Hq * Sq, 16));
   const dim3 g_dq((unsigned)((int64_t)p.num_m * B * Hq));
-  const dim3 g_dkdv((unsigned)((int64_t)p.num_n * B * Hkv));
+  const dim3 g_dkdv((unsigned)((int64_t)p.num_n * B * Hkv)), block_dkdv(512);
   if (d == 128) {
     hipLaunchKernelGGL(ff::attn_bwd_prep<128>, g_prep, block, 0, s, p);
     if (causal) {
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, true>), g_dkdv, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, true>), g_dkdv, block_dkdv, 0, s, p);
       hipLaunchKernelGGL((ff::attn_bwd_dq<128, true>), g_dq, block, 0, s, p);
     } else {
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, false>), g_dkdv, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, false>), g_dkdv, block_dkdv, 0, s, p);
       hipLaunchKernelGGL((ff::attn_bwd_dq<128, false>), g_dq, block, 0, s, p);
     }
   } else {
     hipLaunchKernelGGL(ff::attn_bwd_prep<64>, g_prep, block, 0, s, p);
     if (causal) {
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, true>), g_dkdv, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, true>), g_dkdv, block_dkdv, 0, s, p);
       hipLaunchKernelGGL((ff::attn_bwd_dq<64, true>), g_dq, block, 0, s, p);
     } else {
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, false>), g_dkdv, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, false>), g_dkdv, block_dkdv, 0, s, p);
       hipLaunchKernelGGL((ff::attn_bwd_dq<64, false>), g_dq, block, 0, s, p);
     }
   }
