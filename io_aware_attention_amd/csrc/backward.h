@@ -244,33 +244,37 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
   const float c2 = p.scale_log2;
   const int last_key = CAUSAL && qrow + Sk - Sq < Sk - 1 ? qrow + Sk - Sq : Sk - 1;
 
-  issue(0);
-  wait_vmem();
-  __syncthreads();
-  for (int t = 0; t < n_max; ++t) {
+  // one key tile; PAR = t % 2 selects its K and V buffers at compile time, so every LDS
+  // access is a per-lane offset plus an immediate
+  const uint32_t lds0 = lds_addr(smem);
+  auto step = [&](auto PARC, int t) {
+    constexpr uint32_t PAR = decltype(PARC)::value;
+    constexpr uint32_t K_OFF = PAR * TILE, V_OFF = (2 + PAR) * TILE;
     if (t + 1 < n_max) issue(t + 1);  // into the other buffers, free since the last barrier
-    const uint32_t kl = smem_addr + (t & 1) * TILE;
-    const uint32_t vl = smem_addr + (2 + (t & 1)) * TILE;
     // per 32-key block kb: S^T = K Q^T and dP^T = V dO^T, dS^T = P^T (dP^T - D) with
     // P^T = 2^(s c2 - L2) (masked keys give 0), then dQ^T += K^T dS^T through transposing
     // reads of the K tile
     const bool masked = t >= n_mask;
-    const int vis = last_key - t * BN - 8 * H;  // key offsets <= vis are visible
     static_for<2>([&](auto KB) {
       constexpr int kb = decltype(KB)::value;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
-        s = mfma32(lds_b128(kl + ad.row[c] + kb * 32 * ROWB), qf[c], s);
-        dp = mfma32(lds_b128(vl + ad.row[c] + kb * 32 * ROWB), of[c], dp);
+        s = mfma32(lds_b128(lds0 + K_OFF + kb * 32 * ROWB + ad.row[c]), qf[c], s);
+        dp = mfma32(lds_b128(lds0 + V_OFF + kb * 32 * ROWB + ad.row[c]), of[c], dp);
+      }
+      float pr[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pr[e] = fast_exp2(__builtin_fmaf(s[e], c2, -L2));
+      if (masked) {
+        const int vis = last_key - t * BN - 8 * H - 32 * kb;  // key offsets <= vis are visible
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (perm_row(e) > vis) pr[e] = 0.f;
       }
       float ds[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float pr = fast_exp2(__builtin_fmaf(s[e], c2, -L2));
-        if (masked && 32 * kb + perm_row(e) > vis) pr = 0.f;
-        ds[e] = pr * (dp[e] - Dr);
-      }
+      for (int e = 0; e < 16; ++e) ds[e] = pr[e] * (dp[e] - Dr);
       u32x4 dsf[2];
 #pragma unroll
       for (int cp = 0; cp < 2; ++cp)
@@ -281,12 +285,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
         constexpr int off = (32 * kb + 16 * cp) * ROWB;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          dqacc[db] = mfma32(tr_operand<off>(kl, ad.tlo[db], ad.thi[db]), dsf[cp], dqacc[db]);
+          dqacc[db] = mfma32(tr_operand<off>(lds0 + K_OFF, ad.tlo[db], ad.thi[db]), dsf[cp], dqacc[db]);
       });
     });
     wait_vmem();
     __syncthreads();
+  };
+
+  issue(0);
+  wait_vmem();
+  __syncthreads();
+  int t = 0;
+  for (; t + 1 < n_max; t += 2) {
+    step(std::integral_constant<uint32_t, 0>{}, t);
+    step(std::integral_constant<uint32_t, 1>{}, t + 1);
   }
+  if (t < n_max) step(std::integral_constant<uint32_t, 0>{}, t);
 
   // dQ = scale * dQ^T: element 4j + i of block db is dcol 32db + 8j + 4H + i
   if (qrow < Sq) {
