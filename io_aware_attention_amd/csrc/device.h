@@ -116,8 +116,16 @@ __device__ __forceinline__ void buffer_load_lds16(i32x4 desc, uint32_t voff, uin
                : "memory", "m0");
 }
 
-// All of this wave's vector-memory loads (including loads into LDS) have completed.
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// All of this wave's vector-memory loads (including loads into LDS) have completed.  The
+// inline wait covers the loads the compiler cannot see (the buffer loads into LDS); the
+// builtin one after it tells the compiler's own wait tracking that its loads are done too.
+// Without that, a compiler load still pending in its model (a scale, say) gets a vmcnt(n)
+// at its first use, and by then the counter also holds the next tile's loads into LDS:
+// the wait would stall on the prefetch.
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
+}
 
 __device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
 
