@@ -48,7 +48,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {k: [os.path.join(ROOT, "io_aware_attention_amd", "csrc", f) for f in v]
                   for k, v in {"attn_fwd_prefill": ("device.h", "prefill.h"),
                                "attn_fwd_splitkv": ("device.h", "splitkv.h"),
-                               "attn_bwd_dkdv": ("device.h", "backward.h")}.items()}
+                               "attn_bwd_dkdv": ("device.h", "backward.h"),
+                               "attn_fwd_fp8": ("device.h", "fp8.h")}.items()}
 
 
 def log(*a):
