@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8(Fp8Params p) {
       qf[c].lo = qrow < Sq ? ld16(qp + 64 * c) : z;
       qf[c].hi = qrow < Sq ? ld16(qp + 64 * c + 16) : z;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // in flight with the first K and V tiles; the first step's wait_vmem() retires them
   }
 
   // ---- direct HBM -> LDS loads of K and V tiles (as the bf16 kernel, 1-byte elements)

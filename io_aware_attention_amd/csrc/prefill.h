@@ -254,9 +254,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
       if (qrow < Sq) qf[c] = ld16(qp + 16 * c);
       else qf[c] = u32x4{0u, 0u, 0u, 0u};
     }
-    // Retire the Q loads here, visibly to the compiler, so that it does not wait on
-    // vector memory inside the key loop (where the K/V loads are in flight).
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // The Q loads stay in flight while the first K and V tiles are issued; the
+    // wait_vmem() before the key loop retires both, visibly to the compiler (whose
+    // tracking would otherwise put a wait inside the loop, behind the K/V prefetch).
   }
 
   // ---- direct HBM -> LDS loads.  Wave w, load k fills the 1 KiB LDS block
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
   issue_k(t);
   issue_v(t);
   issue_k(t - 1);
-  wait_vmem();  // this wave's share of the tiles is in LDS
+  wait_vmem();  // Q in registers, this wave's share of the tiles in LDS
   __syncthreads();
   // Scores of two consecutive tiles: in a step of parity P, S[P] holds tile t's and
   // S[P ^ 1] receives tile t-1's; the roles swap every step, so nothing is copied.
