@@ -148,8 +148,16 @@ struct Fp8Traits {
   static constexpr int kLds = 4 * TILE;
   static constexpr int RPB = 256 / ROWB;           // rows per 256-byte bank line
   static constexpr int LOADS = BN * CPR / kThreads;
-  // swizzle: physical chunk = logical chunk ^ key(row); rows 16 apart share a key
-  static __device__ __forceinline__ int key(int r) { return (r / RPB) % CPR; }
+  // swizzle: physical chunk = logical chunk ^ key(row); rows 16 apart share a key.  Banks
+  // span 256-byte lines (RPB rows); a 128-bit read serves 16 lanes (16 consecutive rows,
+  // one logical chunk), a transposing read 32 lanes (rows {0..3, 8..11} + 4H of a 16-row
+  // group, two adjacent chunks).  The key of line u must be one-to-one for the first and
+  // spread the rows 0, 2, 8, 10 (lines 0, 1, 4, 5) over distinct chunk pairs for the second:
+  // at d = 128 it is u with bits 0 and 1 swapped; at d = 64 (four rows a line) u itself.
+  static __device__ __forceinline__ int key(int r) {
+    const int u = (r / RPB) % CPR;
+    return CPR == 8 ? ((u & 4) | ((u & 1) << 1) | ((u >> 1) & 1)) : u;
+  }
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
