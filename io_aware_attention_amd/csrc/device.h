@@ -96,6 +96,10 @@ __device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t a) {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Cache-policy operand of the buffer-load builtins: the non-temporal hint (the nt bit),
+// for data read exactly once, such as the key/value stream of a decode step.
+constexpr int kLoadStreaming = 2;
+
 // Buffer descriptor (gfx9 layout: base, stride 0, num_records bytes, raw dword3).
 // Reads at byte offsets >= num_records return zero.
 __device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t num_records) {

@@ -137,8 +137,12 @@ struct PrefillTraits {
   static __device__ __forceinline__ int vkey(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
 };
 
+// Occupancy: two workgroups per CU at d = 128 (256 VGPRs); three at d = 64, where the
+// kernel fits the 168 VGPRs that three waves per SIMD allow (32 KiB of LDS each).  A
+// third slot per CU shortens the second, partly filled round of workgroups that grids
+// slightly above 512 leave (2 x 5000 x 8 at d = 64: 640 workgroups).
 template <int D, bool CAUSAL, int VAR>
-__global__ __launch_bounds__(256, 2) void attn_fwd_prefill(FwdParams p) {
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist for the device target only
   constexpr bool WIN = VAR & kVarWindow, ALIBI = VAR & kVarAlibi, CAP = VAR & kVarSoftcap;
   constexpr bool LOGIT = ALIBI || CAP;  // scores become base-2 logits before the row max
