@@ -13,6 +13,8 @@
 #include "flashfwd.h"
 #include "prefill.h"
 #include "splitkv.h"
+#include "combine.h"
+#include "append.h"
 #include "backward.h"
 #include "fp8.h"
 

@@ -1,7 +1,6 @@
-// attn_fwd_splitkv and attn_splitkv_combine: the split-KV forward pass for
-// short query blocks (decode), and the LSE-weighted combine of its partials
-// ("03 forward CUDA kernel", section 7; the walk-through's split-KV kernel and
-// grid description).
+// attn_fwd_splitkv: the split-KV forward pass for short query blocks (decode),
+// whose partials attn_splitkv_combine (combine.h) merges ("03 forward CUDA
+// kernel", section 7; the walk-through's split-KV kernel and grid description).
 //
 // A workgroup owns one (block of 16 folded query rows, batch, key/value head,
 // split).  The Hq/Hkv query heads that share a key/value head are folded into
@@ -76,8 +75,18 @@ struct SplitTraits {
   static constexpr int BMD = 16;                  // folded rows per workgroup
   static constexpr int TK = 32;                   // keys per wavefront step
   static constexpr int kWaves = 4;
-  static constexpr int VS = TK * 2 + 16;          // V^T row stride in LDS, bytes
-  static constexpr int WV = D * VS;               // V^T area per wavefront
+  // V^T layout in a wavefront's LDS area: dcol j, 16-byte chunk ch (keys 8 ch .. +7) at
+  //   GS (j >> 3) + 64 (j & 7) + 16 (ch ^ (((j >> 2) ^ ((j >> 5) << SH)) & 3)),
+  // SH = 1 at d = 64, else 0.  Each group of 8 dcol rows (64 bytes each) is padded to
+  // GS = 576 bytes, so the groups start at four different bank offsets, and the chunk
+  // XOR spreads the rows that share an offset over the row.  The transposing writes (per
+  // lane 8 dcols of 4 keys: eight 8-byte writes to dcol rows 8 apart) then reach every
+  // LDS bank twice, the minimum, where plain 80-byte rows put 16 lanes on two bank
+  // offsets (an 8-way conflict); the 16-byte reads of GEMM1 stay conflict-free.  Row
+  // offsets within a group are additive, so they fold into the instructions' offsets.
+  static constexpr int GS = 576;
+  static constexpr int SH = D == 64 ? 1 : 0;
+  static constexpr int WV = (D / 8) * GS;          // V^T area per wavefront
   static constexpr int VB = TK * D / 8 / 4 / 64;  // 4-key x 8-dcol V blocks per lane
   static constexpr int kCombine = kWaves * (2 * BMD + BMD * D) * 4;
   static constexpr int kLds = kWaves * WV > kCombine ? kWaves * WV : kCombine;
@@ -90,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   constexpr bool LOGIT = ALIBI || CAP;  // scores become base-2 logits before the row max
   static_assert(VAR == 0 || CACHE, "variants are built for the cache kernel");
   using T = SplitTraits<D>;
-  constexpr int TK = T::TK, VS = T::VS, VB = T::VB, NW = T::kWaves;
+  constexpr int TK = T::TK, VB = T::VB, NW = T::kWaves;
   __shared__ __attribute__((aligned(16))) char smem[T::kLds];
 
   int u = blockIdx.x;
@@ -200,6 +209,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   const uint16_t* kbase = p.k + brow * kv_stride + (int64_t)hk * D;
   const uint16_t* vbase = p.v + brow * kv_stride + (int64_t)hk * D;
   char* wv = smem + wave * T::WV;
+  // V^T addresses (the layout in SplitTraits).  Writes: base of dcols 8 cg + 4 h .. + 3
+  // of this lane's key block; dcol 8 cg + c is at vt_w[bi][c >> 2] + 64 (c & 3).  Reads
+  // (GEMM1's A operand, dcol 16 db + nr, chunk g4): 2 GS db + vt_r[chunk key of db].
+  int vt_w[VB][2];
+#pragma unroll
+  for (int bi = 0; bi < VB; ++bi) {
+    const int blk = lane + 64 * bi;
+    const int cg = blk % (D / 8), kg = blk / (D / 8);
+    const int k0 = ((2 * cg) ^ ((cg >> 2) << T::SH)) & 3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      vt_w[bi][h] = T::GS * cg + 256 * h + 16 * ((kg >> 1) ^ k0 ^ h) + 8 * (kg & 1);
+  }
+  int vt_r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    vt_r[k] = T::GS * (nr >> 3) + 64 * (nr & 7) + 16 * (g4 ^ ((nr >> 2) & 3) ^ k);
 
   f32x4 oacc[D / 16];
 #pragma unroll
@@ -313,11 +339,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
     for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
     const u32x4 pf = pack8(sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1],
                            sc[1][2], sc[1][3]);
-    // V -> V^T in this wavefront's LDS area
+    // V -> V^T in this wavefront's LDS area: dcol 8 cg + c of keys 4 kg .. 4 kg + 3
 #pragma unroll
     for (int bi = 0; bi < VB; ++bi) {
-      const int blk = lane + 64 * bi;
-      const int cg = blk % (D / 8), kg = blk / (D / 8);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int dw = c >> 1;
@@ -329,14 +353,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
           val[0] = lo_lo(vreg[bi][0][dw], vreg[bi][1][dw]);
           val[1] = lo_lo(vreg[bi][2][dw], vreg[bi][3][dw]);
         }
-        *reinterpret_cast<u32x2*>(wv + (8 * cg + c) * VS + 8 * kg) = val;
+        *reinterpret_cast<u32x2*>(wv + vt_w[bi][c >> 2] + 64 * (c & 3)) = val;
       }
     }
     wave_lds_sync();
     // O^T += V^T . P^T; A operand: V^T[16 db + nr][8 g4 .. +7]
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(wv + (16 * db + nr) * VS + 16 * g4);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(
+          wv + 2 * T::GS * db + vt_r[((db >> 1) << T::SH) & 3]);
       oacc[db] = mfma16(a, pf, oacc[db]);
     }
     wave_lds_sync();
@@ -420,94 +445,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
     if ((tid & 15) == 0) *ldst = lse_val;
   }
 #endif
-}
-
-struct CombineParams {
-  const float* o_accum;
-  const float* lse_accum;
-  float* o;
-  float* lse;
-  int B, Sq, Hq, num_splits;
-  int rows;  // B * Hq * Sq
-};
-
-// One wavefront per (batch, head, query) row; lanes cover the head dimension.
-template <int D>
-__global__ __launch_bounds__(256) void attn_splitkv_combine(CombineParams p) {
-  constexpr int DPL = D / 64;  // dcols per lane
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= p.rows) return;
-  const int64_t split_stride = (int64_t)p.rows;
-  float M = -INFINITY;
-  for (int s = 0; s < p.num_splits; ++s) M = vmax(M, p.lse_accum[s * split_stride + row]);
-  const int i = row % p.Sq;
-  const int bh = row / p.Sq;
-  const int h = bh % p.Hq, b = bh / p.Hq;
-  float* orow = p.o + (((int64_t)b * p.Sq + i) * p.Hq + h) * D + lane * DPL;
-  if (M == -INFINITY) {
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) orow[c] = 0.f;
-    if (lane == 0) p.lse[row] = -INFINITY;
-    return;
-  }
-  float sum = 0.f;
-  for (int s = 0; s < p.num_splits; ++s)
-    sum += fast_exp2((p.lse_accum[s * split_stride + row] - M) * kLog2e);
-  const float L = M + fast_log2(sum) * kLn2;
-  float acc[DPL];
-#pragma unroll
-  for (int c = 0; c < DPL; ++c) acc[c] = 0.f;
-  for (int s = 0; s < p.num_splits; ++s) {
-    const float w = fast_exp2((p.lse_accum[s * split_stride + row] - L) * kLog2e);
-    const float* src = p.o_accum + (s * split_stride + row) * D + lane * DPL;
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) acc[c] += w * src[c];
-  }
-#pragma unroll
-  for (int c = 0; c < DPL; ++c) orow[c] = acc[c];
-  if (lane == 0) p.lse[row] = L;
-}
-
-// Writes new keys and values into a key/value cache laid out as for the CACHE split
-// kernel: row t of batch b goes to logical position cache_seqlens[b] + t ("03 forward
-// CUDA kernel", section 8: new tokens are appended to the cache in place before the
-// attention reads it).  Positions past the cache's capacity are dropped.  One thread per
-// 16-byte chunk of a (batch, new row, kv head) row, K and V both.
-struct AppendParams {
-  const uint16_t* k_new;
-  const uint16_t* v_new;
-  uint16_t* k_cache;
-  uint16_t* v_cache;
-  const int* seqlens;
-  const int* block_table;
-  int B, S_new, Hkv, num_blocks, page, max_blocks;
-  int64_t chunks;  // B * S_new * Hkv * D / 8
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_kvcache_append(AppendParams p) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per head row
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= p.chunks) return;
-  const int c = (int)(i % CPR);
-  int64_t r = i / CPR;
-  const int h = (int)(r % p.Hkv);
-  r /= p.Hkv;
-  const int t = (int)(r % p.S_new);
-  const int b = (int)(r / p.S_new);
-  const int cap = p.max_blocks * p.page;
-  int n0 = p.seqlens[b];
-  n0 = n0 < 0 ? 0 : (n0 > cap ? cap : n0);
-  const int pos = n0 + t;  // cap + S_new fits in an int (host check)
-  if (pos >= cap) return;
-  const int pg = pos / p.page;
-  int blk = p.block_table ? p.block_table[(int64_t)b * p.max_blocks + pg] : b;
-  blk = blk < 0 ? 0 : (blk >= p.num_blocks ? p.num_blocks - 1 : blk);
-  const int64_t dst = (((int64_t)blk * p.page + (pos - pg * p.page)) * p.Hkv + h) * D + 8 * c;
-  const int64_t src = (((int64_t)b * p.S_new + t) * p.Hkv + h) * D + 8 * c;
-  st16(p.k_cache + dst, ld16(p.k_new + src));
-  st16(p.v_cache + dst, ld16(p.v_new + src));
 }
 
 }  // namespace ff
