@@ -65,6 +65,26 @@ def test_splitkv_partials_and_combine(ff, oracle, shape, num_splits):
                 assert np.all(oa[s] == 0.0) and np.all(np.isneginf(la[s]))
 
 
+@pytest.mark.parametrize("num_splits", [63, 64, 65, 100, 128])
+def test_splitkv_many_splits(ff, oracle, num_splits):
+    # The combine loads the LSEs of splits l and l + 64 in lane l: split counts around and
+    # past 64, up to the largest allowed.  20000 keys are 157 key blocks, so at these
+    # counts a third or more of the splits are empty (0, -inf).
+    B, Sq, Sk, Hq, Hkv, d, causal = 2, 1, 20000, 8, 2, 128, False
+    say(f"splitkv many splits S={num_splits}")
+    q, k, v = make_inputs(B, Sq, Sk, Hq, Hkv, d, seed=1700 + num_splits)
+    scale = synth.f32(1 / math.sqrt(d))
+    o, lse, oa, la = run_split(ff, q, k, v, causal, scale, num_splits)
+    op_ref, lp_ref, o_ref, lse_ref = oracle.split(q, k, v, causal, scale, BLOCK_N, num_splits)
+    check_outputs(o, lse, o_ref, lse_ref, f"S={num_splits} combined")
+    check_outputs(oa, la, op_ref, lp_ref, f"S={num_splits} partials")
+    per = -(-(-(-Sk // BLOCK_N)) // num_splits)
+    empty = [s for s in range(num_splits) if s * per >= -(-Sk // BLOCK_N)]
+    assert empty, "the case should hold empty splits"
+    for s in empty:
+        assert np.all(oa[s] == 0.0) and np.all(np.isneginf(la[s]))
+
+
 def test_gqa_decode_workload_all_rows(ff, oracle):
     import torch
     w = synth.WORKLOADS["gqa_decode"]
