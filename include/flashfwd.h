@@ -258,7 +258,7 @@ long long attn_bwd_workspace_floats(int B, int Sq, int Hq);
  * P and dS are rounded to bf16 as matrix-core operands; all accumulation is fp32.  The
  * result is bitwise deterministic (no atomics).  Argument rules and errors as for
  * attn_fwd (dq, dk, dv and ws must not overlap each other or any input:
- * FF_ERR_ALIAS).  Enqueues three kernels on `stream`. */
+ * FF_ERR_ALIAS).  Enqueues two kernels on `stream`. */
 int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
              const void* dout, float* dq, float* dk, float* dv, float* ws, int B, int Sq, int Sk,
              int Hq, int Hkv, int d, int causal, float scale, void* stream);

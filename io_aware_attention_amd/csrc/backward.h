@@ -4,13 +4,15 @@
 // stored but recomputed from the saved LSE, P = exp(scale * q.k - LSE); with the row
 // scalar D = sum_c dO_c O_c,
 //   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
-// Masked pairs have P = dS = 0.  Three kernels, all deterministic (no atomics):
-//   attn_bwd_prep  D and the base-2 LSE per row (memory-bound, 16 lanes per row)
+// Masked pairs have P = dS = 0.  Two kernels, in this order, both deterministic (no
+// atomics):
 //   attn_bwd_dq    one workgroup per 128-query tile, key/value tiles streamed
-//                  through LDS: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T
+//                  through LDS: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T; its
+//                  prologue also computes D and the base-2 LSE of its rows and
+//                  stores them in the workspace
 //   attn_bwd_dkdv  one workgroup per 128 keys of a key/value head, query tiles of
-//                  every query head of the group streamed through LDS:
-//                  S = Q K^T, dV^T += dO^T P, dP = dO V^T, dK^T += Q^T dS
+//                  every query head of the group (and their D, LSE) streamed through
+//                  LDS: S = Q K^T, dV^T += dO^T P, dP = dO V^T, dK^T += Q^T dS
 // The products use v_mfma_f32_32x32x16_bf16; P and dS are rounded to bf16 (RNE) as
 // MFMA operands, everything else stays fp32.  The dQ kernel is the forward kernel's
 // mirror image (key rows permuted so that scores are the next product's B operand);
@@ -40,33 +42,6 @@ struct BwdParams {
   float scale;       // softmax scale: enters dQ and dK
   float scale_log2;  // scale * log2(e)
 };
-
-// ---- attn_bwd_prep: D = sum_c dO_c O_c and the base-2 LSE, one row per 16 lanes.
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_prep(BwdParams p) {
-  constexpr int E = D / 16;  // columns per lane
-  const int rows = p.B * p.Hq * p.Sq;
-  const int r = blockIdx.x * 16 + (threadIdx.x >> 4);  // row in [B, Hq, Sq] order
-  const int sub = threadIdx.x & 15;
-  if (r >= rows) return;  // all 16 lanes of a row leave together
-  const int i = r % p.Sq, bh = r / p.Sq;
-  const int h = bh % p.Hq, b = bh / p.Hq;
-  const int64_t base = (((int64_t)b * p.Sq + i) * p.Hq + h) * D + sub * E;
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    acc += __uint_as_float((uint32_t)p.dout[base + e] << 16) * p.o[base + e];
-  acc += __shfl_xor(acc, 8);
-  acc += __shfl_xor(acc, 4);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 1);
-  if (sub == 0) {
-    const int64_t w = (int64_t)bh * p.sq_pad + i;
-    p.dsum[w] = acc;
-    const float l = p.lse[r];
-    p.lse2[w] = l == -INFINITY ? INFINITY : l * kLog2e;
-  }
-}
 
 // Shared geometry of the two main kernels: 4 wavefronts of 32 rows, tiles of T rows
 // of the streamed tensors, row-major in LDS with the 16-byte chunks of each row
@@ -194,6 +169,49 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
   const int64_t q_stride = (int64_t)p.Hq * D;
   const int kv_row_bytes = p.Hkv * D * 2;
   float* dq_row = p.dq + ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D;
+
+  // Resident dO^T fragments [qrow][16c + 8H .. +7], and the row scalars: D = sum_c dO_c
+  // O_c (this lane's half of the columns, then the other half from lane l ^ 32) and
+  // L2 = LSE log2(e) (+inf for a row with no visible key).  They go to the workspace for
+  // the dK/dV kernel, which runs next.  Every row below Sq is written, also in tiles that
+  // see no key, since that kernel multiplies P = 0 by (dP - D).
+  // The Q^T fragments (resident too) are loaded alongside, so that all three tensors'
+  // loads are in flight together.
+  const int64_t off = ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D + 8 * H;
+  const bool in = qrow < Sq;
+  u32x4 of[D / 16], qf[D / 16];
+  float L2 = INFINITY, Dr = 0.f;
+  {
+    f32x4 ov[D / 16][2];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      of[c] = in ? ld16(p.dout + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      ov[c][0] = in ? *reinterpret_cast<const f32x4*>(p.o + off + 16 * c) : f32x4{};
+      ov[c][1] = in ? *reinterpret_cast<const f32x4*>(p.o + off + 16 * c + 4) : f32x4{};
+    }
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qf[c] = in ? ld16(p.q + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+    float part[2] = {0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // bf16 pair e: element 2e (low half), 2e + 1 (high)
+        const f32x4& o = ov[c][e >> 1];
+        part[0] += __uint_as_float(of[c][e] << 16) * o[2 * (e & 1)];
+        part[1] += __uint_as_float(of[c][e] & 0xffff0000u) * o[2 * (e & 1) + 1];
+      }
+    Dr = sum_xor32(part[0] + part[1]);
+    if (qrow < Sq) {
+      const float l = p.lse[((int64_t)b * p.Hq + h) * Sq + qrow];
+      L2 = l == -INFINITY ? INFINITY : l * kLog2e;
+      if (H == 0) {
+        const int64_t r = ((int64_t)b * p.Hq + h) * p.sq_pad + qrow;
+        p.dsum[r] = Dr;
+        p.lse2[r] = L2;
+      }
+    }
+  }
   if (n_max <= 0) {  // no visible key for any row of this tile: dQ = 0
     if (qrow < Sq) {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -202,23 +220,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
     return;
   }
 
-  // resident Q^T and dO^T fragments: [qrow][16c + 8H .. +7]; this row's L2 and D
-  u32x4 qf[D / 16], of[D / 16];
-  float L2 = INFINITY, Dr = 0.f;
-  {
-    const int64_t off = ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D + 8 * H;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      qf[c] = qrow < Sq ? ld16(p.q + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-      of[c] = qrow < Sq ? ld16(p.dout + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (qrow < Sq) {
-      const int64_t r = ((int64_t)b * p.Hq + h) * p.sq_pad + qrow;
-      L2 = p.lse2[r];
-      Dr = p.dsum[r];
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours in flight in the loop
-  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours in flight in the loop
 
   const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)b * Sk * p.Hkv + hk) * D * 2;
   const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)b * Sk * p.Hkv + hk) * D * 2;

@@ -232,27 +232,26 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
   p.scale = scale;
   p.scale_log2 = scale * ff::kLog2e;
   hipStream_t s = (hipStream_t)stream;
+  // dQ first: its prologue writes each row's D and base-2 LSE into ws, which the dK/dV
+  // kernel reads
   const dim3 block(256);
-  const dim3 g_prep((unsigned)cdiv((int64_t)B * Hq * Sq, 16));
   const dim3 g_dq((unsigned)((int64_t)p.num_m * B * Hq));
   const dim3 g_dkdv((unsigned)((int64_t)p.num_n * B * Hkv)), block_dkdv(512);
   if (d == 128) {
-    hipLaunchKernelGGL(ff::attn_bwd_prep<128>, g_prep, block, 0, s, p);
     if (causal) {
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, true>), g_dkdv, block_dkdv, 0, s, p);
       hipLaunchKernelGGL((ff::attn_bwd_dq<128, true>), g_dq, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, true>), g_dkdv, block_dkdv, 0, s, p);
     } else {
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, false>), g_dkdv, block_dkdv, 0, s, p);
       hipLaunchKernelGGL((ff::attn_bwd_dq<128, false>), g_dq, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, false>), g_dkdv, block_dkdv, 0, s, p);
     }
   } else {
-    hipLaunchKernelGGL(ff::attn_bwd_prep<64>, g_prep, block, 0, s, p);
     if (causal) {
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, true>), g_dkdv, block_dkdv, 0, s, p);
       hipLaunchKernelGGL((ff::attn_bwd_dq<64, true>), g_dq, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, true>), g_dkdv, block_dkdv, 0, s, p);
     } else {
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, false>), g_dkdv, block_dkdv, 0, s, p);
       hipLaunchKernelGGL((ff::attn_bwd_dq<64, false>), g_dq, block, 0, s, p);
+      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, false>), g_dkdv, block_dkdv, 0, s, p);
     }
   }
   return launch_status();
