@@ -387,13 +387,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8(Fp8Params p) {
       for (int e = 0; e < 16; ++e) mx = vmax(mx, sc[kb][e]);
     return max_xor32(mx);
   };
-  // Per-tile constants: exponent factor, log2(sv / sv_max), sv_max / sv.
+  // Per-tile constants: exponent factor, log2(sv / sv_max), sv_max / sv.  The last two
+  // only scale probabilities, so the hardware log2 and reciprocal (about 1 ulp) serve;
+  // IEEE divisions cost ~20 vector instructions per tile in a loop bound by vector work.
   struct TileScale {
     float c2, lr, ir;
   };
+  const float inv_sv_max = 1.f / sv_max;
   auto tile_scale = [&](int t) {
-    const float sk = ks[t >> 1], sv = vs[t >> 1];
-    return TileScale{c2q * sk, fast_log2(sv / sv_max), sv_max / sv};
+    const float sk = ks[t >> 1], r = vs[t >> 1] * inv_sv_max;
+    return TileScale{c2q * sk, fast_log2(r), __builtin_amdgcn_rcpf(r)};
   };
 
   // ---- key loop, tiles n_max-1 down to 0: K and V of tile t-1 load while tile t is
