@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8(Fp8Params p) {
     // p~ = 2^(s c2 - m + lr): the V block's scale ratio rides in the exponent
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     const float off = ts.lr - m_use;
-    float lsum[2] = {0.f, 0.f};
+    float lsum[2] = {-0.f, -0.f};  // -0: the first adds fold away
     Frag32 pb;
     static_for<8>([&](auto W) {  // four probabilities -> one dword of the B operand
       constexpr int w = decltype(W)::value, e0 = 4 * w;

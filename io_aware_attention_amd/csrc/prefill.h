@@ -458,7 +458,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
       kr[0] = kread(0);
       kr[1] = kread(1);
     }
-    float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+    // partial row sums start at -0, the exact additive identity, so the first add of
+    // each folds away (0 + x cannot be folded under IEEE rules: -0 + 0 = +0)
+    float lsum[4] = {-0.f, -0.f, -0.f, -0.f};
     u32x4 pf[2][2];
     static_for<NG0>([&](auto I) {
       constexpr int i = decltype(I)::value;

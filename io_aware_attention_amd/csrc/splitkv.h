@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
-    float ls = 0.f;
+    float ls = -0.f;  // -0: the first add folds away
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
