@@ -51,28 +51,39 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_quantize_fp8(QuantParams p) {
   constexpr int E = D / 64;    // elements per lane per row
   constexpr int RPW = 32;      // rows per wavefront
+  // head innermost: consecutive workgroups read the heads of the same 128 rows, one
+  // contiguous region of 128 * H * D * 2 bytes, instead of 256-byte pieces of rows
+  // H * D * 2 bytes apart
   const int u = blockIdx.x;
-  const int blk = u % p.nblk;
-  const int h = (u / p.nblk) % p.H;
+  const int h = u % p.H;
+  const int blk = (u / p.H) % p.nblk;
   const int b = u / (p.nblk * p.H);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r0 = blk * 128 + wave * RPW;
   __shared__ float wmax[4];
 
+  // All 32 row loads are issued before any is used (rows past S read row 0 and are
+  // zeroed afterwards): a load under a condition became a branch with its own wait,
+  // which serialised 32 memory latencies per wavefront.
+  uint32_t raw[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int row = r0 + r < p.S ? r0 + r : 0;
+    const int64_t off = (((int64_t)b * p.S + row) * p.H + h) * D + E * lane;
+    if constexpr (E == 2) raw[r] = *reinterpret_cast<const uint32_t*>(p.x + off);
+    else raw[r] = p.x[off];
+  }
   float y[RPW][E];
   float amax = 0.f;
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    const int row = r0 + r;
-    const bool ok = row < p.S;
-    const int64_t off = (((int64_t)b * p.S + (ok ? row : 0)) * p.H + h) * D + E * lane;
+    const uint32_t w = r0 + r < p.S ? raw[r] : 0u;
     float v[E];
     if constexpr (E == 2) {
-      const uint32_t w = ok ? *reinterpret_cast<const uint32_t*>(p.x + off) : 0u;
       v[0] = __uint_as_float(w << 16);
       v[1] = __uint_as_float(w & 0xFFFF0000u);
     } else {
-      v[0] = ok ? __uint_as_float((uint32_t)p.x[off] << 16) : 0.f;
+      v[0] = __uint_as_float(w << 16);
     }
     if (p.rotate) {
       // butterflies of distance 1, 2, ..., D/2 over element index E * lane + k
