@@ -16,6 +16,7 @@
 #include "combine.h"
 #include "append.h"
 #include "backward.h"
+#include "quantize.h"
 #include "fp8.h"
 
 namespace {
