@@ -444,7 +444,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // -- block A: QK^T of tile t-1 interleaved with p = 2^(s c - m) of tile t
+    // -- block A: QK^T of tile t-1 interleaved with p = 2^(s c - m) of tile t.  It runs
+    // at raised wave priority and block B at the base one: when the two wavefronts of a
+    // SIMD compete, the one in the vector-heavy block issues first and the other's
+    // products fill the matrix pipe (causal_prefill +2.5%, long_causal_gqa +3.2%; the
+    // opposite assignment gained nothing).
+    __builtin_amdgcn_s_setprio(1);
     sn[0] = f32x16{};
     sn[1] = f32x16{};
     u32x4 kr[3];
@@ -487,6 +492,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
     l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
     // -- block B: PV of tile t interleaved with mask and row max of tile t-1
+    __builtin_amdgcn_s_setprio(0);
     const uint32_t vl = smem_addr + (2 + P) * TILE;  // V of tile t
     u32x2 flo[3], fhi[3];
     gemm1_read<0, D, ROWB>(vl, va, flo[0], fhi[0]);
