@@ -76,7 +76,7 @@ class Oracle:
         lib.oracle_attn_online.argtypes = _COMMON + [_I, _P, _P]
         lib.oracle_attn_split.argtypes = _COMMON + [_I, _I, _P, _P, _P, _P]
         lib.oracle_attn_bwd.argtypes = _COMMON + [_P, _P, _P, _P, _P, _P, _P, _P, _P]
-        for f in _FWD_FUNCS:
+        for f in _FWD_FUNCS + ("oracle_attn_bwd",):
             ext = getattr(lib, f + "_ext")
             ext.argtypes = _COMMON + _OPTS + getattr(lib, f).argtypes[len(_COMMON):]
             ext.restype = ctypes.c_int
@@ -197,9 +197,10 @@ class Oracle:
                     lse.ctypes.data])
         return op, lp, o, lse
 
-    def bwd(self, q, k, v, dout, causal, scale, units=None):
+    def bwd(self, q, k, v, dout, causal, scale, units=None, window=None, alibi=None):
         """units: None (all) or an iterable of (b, hk) key/value units to compute; the
-        other units' slices of every output stay zero."""
+        other units' slices of every output stay zero.  window (left, right) and alibi
+        slopes as for fwd; the soft cap is not covered by the backward."""
         arrs, (B, Sq, Sk, Hq, Hkv, d), a = self._args(q, k, v, causal, scale)
         do_ = np.ascontiguousarray(dout)
         if do_.dtype != arrs[0].dtype or do_.shape != arrs[0].shape:
@@ -214,11 +215,10 @@ class Oracle:
         dv = np.zeros((B, Sk, Hkv, d))
         dsum = np.zeros((B, Hq, Sq))
         dq_a, dk_a, dv_a = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
-        self._ok(self.lib.oracle_attn_bwd(*a, do_.ctypes.data,
-                                          None if umask is None else umask.ctypes.data,
-                                          dq.ctypes.data, dk.ctypes.data,
-                                          dv.ctypes.data, dsum.ctypes.data, dq_a.ctypes.data,
-                                          dk_a.ctypes.data, dv_a.ctypes.data), "bwd")
+        self._call("oracle_attn_bwd", a, (B, Sq, Sk, Hq, Hkv, d), (window, alibi, 0.0),
+                   [do_.ctypes.data, None if umask is None else umask.ctypes.data,
+                    dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, dsum.ctypes.data,
+                    dq_a.ctypes.data, dk_a.ctypes.data, dv_a.ctypes.data])
         return dq, dk, dv, dsum, (dq_a, dk_a, dv_a)
 
     # -- FP8 (explainer, FlashAttention-3 precision section)

@@ -447,11 +447,18 @@ int oracle_attn_split(int in_bf16, const void *q, const void *k, const void *v, 
  * every output is zero.  Each unit is done in the two steps of the page's table: the
  * full P and dS rows of its query heads (rows in parallel; dq and D on the way), then
  * dV = P^T dO and dK = scale dS^T Q (keys in parallel). */
-int oracle_attn_bwd(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
-                    int Sk, int Hq, int Hkv, int d, int causal, double scale, const void *dout,
-                    const int *units, double *dq, double *dk, double *dv, double *dsum,
-                    double *dq_abs, double *dk_abs, double *dv_abs) {
-  SETUP_PROBLEM
+/* The backward with the sliding window and ALiBi.  Both leave the formulas above as they
+ * are: a pair outside the window has P = 0, hence dS = 0, and the ALiBi bias does not
+ * depend on q or k, so dQ and dK take dS as it stands.  The soft cap (whose derivative
+ * 1 - tanh^2 would scale dS) is not covered: softcap != 0 returns 8. */
+int oracle_attn_bwd_ext(int in_bf16, const void *q, const void *k, const void *v, int B,
+                        int Sq, int Sk, int Hq, int Hkv, int d, int causal, double scale,
+                        int window_left, int window_right, const double *alibi,
+                        double softcap, const void *dout, const int *units, double *dq,
+                        double *dk, double *dv, double *dsum, double *dq_abs,
+                        double *dk_abs, double *dv_abs) {
+  if (softcap != 0.0) return 8;
+  SETUP_PROBLEM_OPTS(window_left, window_right, alibi, softcap)
   if (!dout || !dq || !dk || !dv || !dsum) return 1;
   const int G = Hq / Hkv;
   const int64_t nq = (int64_t)B * Sq * Hq * d, nkv = (int64_t)B * Sk * Hkv * d;
@@ -542,6 +549,15 @@ int oracle_attn_bwd(int in_bf16, const void *q, const void *k, const void *v, in
   free(p_all);
   free(ds_all);
   return 0;
+}
+
+int oracle_attn_bwd(int in_bf16, const void *q, const void *k, const void *v, int B, int Sq,
+                    int Sk, int Hq, int Hkv, int d, int causal, double scale, const void *dout,
+                    const int *units, double *dq, double *dk, double *dv, double *dsum,
+                    double *dq_abs, double *dk_abs, double *dv_abs) {
+  return oracle_attn_bwd_ext(in_bf16, q, k, v, B, Sq, Sk, Hq, Hkv, d, causal, scale, -1, -1,
+                             NULL, 0.0, dout, units, dq, dk, dv, dsum, dq_abs, dk_abs,
+                             dv_abs);
 }
 
 /* ---------------------------------------------------------------------------------

@@ -363,17 +363,24 @@ def check_backward_exercise_2(orc):
 
 def check_backward_finite_differences(orc):
     # Independent pin: central differences of the forward oracle's loss <dO, O>
-    # (the explainer's CPU lab compares its gradients the same way).
+    # (the explainer's CPU lab compares its gradients the same way), also with a sliding
+    # window and ALiBi slopes, whose backward is checked against the forward only here.
     h = 1e-5
-    for seed, (B, Sq, Sk, Hq, Hkv, d, causal, scale) in enumerate(
-            ((1, 3, 4, 2, 1, 3, False, 0.6), (1, 5, 3, 2, 2, 2, True, 0.9),
-             (2, 3, 6, 3, 1, 2, True, 0.45), (1, 4, 4, 1, 1, 4, True, 1.3))):
+    for seed, (B, Sq, Sk, Hq, Hkv, d, causal, scale, window, alibi) in enumerate(
+            ((1, 3, 4, 2, 1, 3, False, 0.6, None, None),
+             (1, 5, 3, 2, 2, 2, True, 0.9, None, None),
+             (2, 3, 6, 3, 1, 2, True, 0.45, None, None),
+             (1, 4, 4, 1, 1, 4, True, 1.3, None, None),
+             (1, 6, 7, 2, 1, 3, False, 0.8, (2, 1), None),
+             (1, 5, 6, 2, 2, 2, True, 0.7, (1, 0), [0.5, 0.25]),
+             (2, 4, 5, 2, 1, 2, False, 0.9, None, [[0.3, 0.6], [0.1, 0.2]]))):
         q, k, v = _rand(200 + seed, B, Sq, Sk, Hq, Hkv, d)
         do_ = np.random.default_rng(300 + seed).standard_normal(q.shape)
-        dq, dk, dv, _, _ = orc.bwd(q, k, v, do_, causal, scale)
+        dq, dk, dv, _, _ = orc.bwd(q, k, v, do_, causal, scale, window=window, alibi=alibi)
 
         def loss(qq, kk, vv):
-            return float(np.sum(orc.fwd(qq, kk, vv, causal, scale)[0] * do_))
+            o = orc.fwd(qq, kk, vv, causal, scale, window=window, alibi=alibi)[0]
+            return float(np.sum(o * do_))
 
         for which, grad in ((0, dq), (1, dk), (2, dv)):
             base = [q, k, v]
