@@ -263,6 +263,20 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
              const void* dout, float* dq, float* dk, float* dv, float* ws, int B, int Sq, int Sk,
              int Hq, int Hkv, int d, int causal, float scale, void* stream);
 
+/* attn_bwd for the mask and bias variants of attn_fwd_ex: the sliding window
+ * (window_left, window_right; -1 = no limit on that side) and ALiBi slopes (fp32 on the
+ * device, [Hq] with alibi_batch_stride 0 or [B, Hq] with stride Hq), with the same
+ * meaning as there; o and lse must come from attn_fwd_ex with the same options.  A pair
+ * outside the window has P = 0, and the ALiBi bias does not depend on q or k, so the
+ * formulas of attn_bwd stand.  softcap must be 0 (the soft cap's backward is not
+ * provided): anything else returns FF_ERR_OPTION, as do out-of-range options.  The
+ * slopes must not overlap dq, dk, dv or ws (FF_ERR_ALIAS).  Otherwise as attn_bwd. */
+int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv, float* ws, int B, int Sq,
+                int Sk, int Hq, int Hkv, int d, int causal, int window_left, int window_right,
+                const float* alibi_slopes, int alibi_batch_stride, float softcap, float scale,
+                void* stream);
+
 /* Static description of a status code. */
 const char* attn_status_string(int status);
 

@@ -41,6 +41,12 @@ struct BwdParams {
   int num_n;         // 128-key blocks per (batch, kv head)
   float scale;       // softmax scale: enters dQ and dK
   float scale_log2;  // scale * log2(e)
+  // Variants (VAR of both kernels): window limits (-1 = none), key j visible to query i
+  // iff diag - wl <= j <= diag + wr with diag = i + Sk - Sq; ALiBi slope of (batch b,
+  // query head h) at alibi[b * alibi_bstride + h], bias -slope |diag - j|.
+  int wl, wr;
+  const float* alibi;
+  int alibi_bstride;
 };
 
 // Shared geometry of the two main kernels: 4 wavefronts of 32 rows, tiles of T rows
@@ -129,10 +135,14 @@ __device__ __forceinline__ constexpr int perm_row(int e) {
 }
 
 // ---------------------------------------------------------------------------
-// attn_bwd_dq: one workgroup per (128-query tile, batch, query head).
-template <int D, bool CAUSAL>
+// attn_bwd_dq: one workgroup per (128-query tile, batch, query head).  VAR: the window
+// (and ALiBi) of the forward's variants; the key-tile range is clipped at both ends and
+// tiles below n_bot get the left-edge element mask, as in the forward kernel.
+template <int D, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer builtins exist for the device target only
+  constexpr bool WIN = VAR & kVarWindow, ALIBI = VAR & kVarAlibi;
+  static_assert(VAR == 0 || WIN, "variant kernels include the window");
   constexpr int BM = 128, BN = 64;
   using T = BwdTraits<D, BN>;
   constexpr int ROWB = T::ROWB, CPR = T::CPR, TILE = T::TILE, LOADS = T::LOADS;
@@ -164,6 +174,33 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
     const int first = q0 + Sk - Sq + 1;
     const int tm = first <= 0 ? 0 : first / BN;
     n_mask = tm < n_mask ? tm : n_mask;
+  }
+  // Window: key tiles [n_min, n_max) hold keys some row of the tile sees; tiles below
+  // n_bot hold keys left of the last row's window and need the element mask too.  The
+  // range starts at an even tile, since the buffer parity is t & 1; a tile added that way
+  // lies left of every row's window, below n_bot, so it is masked out entirely.
+  int n_min = 0, n_bot = 0;
+  if constexpr (WIN) {
+    constexpr int LB = 6;  // log2(BN)
+    static_assert((1 << LB) == BN, "BN");
+    const int last_q = (q0 + BM < Sq ? q0 + BM : Sq) - 1;
+    if (p.wr >= 0) {
+      const int64_t lim = (int64_t)last_q + Sk - Sq + p.wr;
+      const int64_t nm = lim < 0 ? 0 : (lim >> LB) + 1;
+      n_max = nm < n_max ? (int)nm : n_max;
+      const int64_t first = (int64_t)q0 + Sk - Sq + p.wr + 1;
+      const int64_t tm = first <= 0 ? 0 : first >> LB;
+      n_mask = tm < n_mask ? (int)tm : n_mask;
+    }
+    if (p.wl >= 0) {
+      const int64_t lo_first = (int64_t)q0 + Sk - Sq - p.wl;
+      const int64_t lo_last = (int64_t)last_q + Sk - Sq - p.wl;
+      n_min = lo_first <= 0 ? 0 : (int)((lo_first >> LB) < nb_total ? lo_first >> LB : nb_total);
+      const int64_t nb = lo_last <= 0 ? 0 : (lo_last + BN - 1) >> LB;
+      n_bot = (int)(nb < n_max ? nb : n_max);
+      n_bot = n_bot > n_min ? n_bot : n_min;
+      n_min &= ~1;
+    }
   }
 
   const int64_t q_stride = (int64_t)p.Hq * D;
@@ -212,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
       }
     }
   }
-  if (n_max <= 0) {  // no visible key for any row of this tile: dQ = 0
+  if (n_max <= n_min) {  // no visible key for any row of this tile: dQ = 0
     if (qrow < Sq) {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       for (int c = H * 4; c < D; c += 8) st16f(dq_row + c, z);
@@ -244,7 +281,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{};
   const float c2 = p.scale_log2;
-  const int last_key = CAUSAL && qrow + Sk - Sq < Sk - 1 ? qrow + Sk - Sq : Sk - 1;
+  int last_key = CAUSAL && qrow + Sk - Sq < Sk - 1 ? qrow + Sk - Sq : Sk - 1;
+  int first_key = 0;  // window: keys below are invisible to this row
+  const int diag = qrow + Sk - Sq;
+  if constexpr (WIN) {
+    if (p.wr >= 0 && (int64_t)diag + p.wr < last_key) last_key = (int)((int64_t)diag + p.wr);
+    if (p.wl >= 0 && (int64_t)diag - p.wl > 0) first_key = (int)((int64_t)diag - p.wl);
+  }
+  // ALiBi slope of this head in base-2 units
+  const float slope2 = ALIBI ? p.alibi[(int64_t)b * p.alibi_bstride + h] * kLog2e : 0.f;
 
   // one key tile; PAR = t % 2 selects its K and V buffers at compile time, so every LDS
   // access is a per-lane offset plus an immediate
@@ -256,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
     // per 32-key block kb: S^T = K Q^T and dP^T = V dO^T, dS^T = P^T (dP^T - D) with
     // P^T = 2^(s c2 - L2) (masked keys give 0), then dQ^T += K^T dS^T through transposing
     // reads of the K tile
-    const bool masked = t >= n_mask;
+    const bool masked = t >= n_mask || (WIN && t < n_bot);
     static_for<2>([&](auto KB) {
       constexpr int kb = decltype(KB)::value;
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -267,12 +312,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
       }
       float pr[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pr[e] = fast_exp2(__builtin_fmaf(s[e], c2, -L2));
+      for (int e = 0; e < 16; ++e) {
+        float x = __builtin_fmaf(s[e], c2, -L2);
+        if constexpr (ALIBI) {  // key t BN + 32 kb + 8 H + perm_row(e)
+          const int key = t * BN + 32 * kb + 8 * H + perm_row(e);
+          x = __builtin_fmaf(-slope2, __builtin_fabsf((float)(diag - key)), x);
+        }
+        pr[e] = fast_exp2(x);
+      }
       if (masked) {
         const int vis = last_key - t * BN - 8 * H - 32 * kb;  // key offsets <= vis are visible
+        const int vlo = first_key - t * BN - 8 * H - 32 * kb;  // and >= vlo (window)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (perm_row(e) > vis) pr[e] = 0.f;
+          if (perm_row(e) > vis || (WIN && perm_row(e) < vlo)) pr[e] = 0.f;
       }
       float ds[16];
 #pragma unroll
@@ -294,10 +347,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
     __syncthreads();
   };
 
-  issue(0);
+  issue(n_min);
   wait_vmem();
   __syncthreads();
-  int t = 0;
+  int t = n_min;
   for (; t + 1 < n_max; t += 2) {
     step(std::integral_constant<uint32_t, 0>{}, t);
     step(std::integral_constant<uint32_t, 1>{}, t + 1);
@@ -333,9 +386,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
 // wavefronts fit on a SIMD.  Each tile costs two workgroup barriers: the one at its
 // start also orders the previous tile's phase 2 before this tile's phase 1, so P and
 // dS need one buffer each.
-template <int D, bool CAUSAL>
+// VAR: the window (and ALiBi): the query-tile range is clipped at both ends and the
+// element mask covers both edges of each key's window.
+template <int D, bool CAUSAL, int VAR>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  constexpr bool WIN = VAR & kVarWindow, ALIBI = VAR & kVarAlibi;
+  static_assert(VAR == 0 || WIN, "variant kernels include the window");
   constexpr int BK = 128, BQ = 64, NT = 512;
   constexpr int ROWB = D * 2, CPR = D / 8, TILE = BQ * ROWB;
   constexpr int LOADS = BQ * CPR / NT;          // 16-byte loads per thread per tile
@@ -363,16 +420,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
   const int dh = wave >> 2;      // phase 2: half of the head dimension
   const int key = k0 + 32 * kb + n;
 
-  // query tiles [qt_lo, num_qt) of each head; tiles below qt_mask need a mask
+  // query tiles [qt_lo, qt_hi) of each head; tiles below qt_mask need the mask of the
+  // right edge (key <= q + Sk - Sq + r: r = 0 when causal, else the window's wr) and
+  // tiles from qt_lmask that of the left edge (key >= q + Sk - Sq - wl)
   const int num_qt = (Sq + BQ - 1) / BQ;
-  int qt_lo = 0, qt_mask = 0;
-  if (CAUSAL) {
-    const int first_q = k0 - (Sk - Sq);  // first query that sees key k0
-    qt_lo = first_q <= 0 ? 0 : (first_q / BQ < num_qt ? first_q / BQ : num_qt);
-    const int q_full = k0 + BK - 1 - (Sk - Sq);  // queries >= q_full see every key of the block
-    qt_mask = q_full <= 0 ? 0 : (q_full + BQ - 1) / BQ;
+  int qt_lo = 0, qt_hi = num_qt, qt_mask = 0, qt_lmask = num_qt;
+  int64_t r_edge = -1;  // -1: no right edge
+  if (CAUSAL) r_edge = 0;
+  else if (WIN && p.wr >= 0) r_edge = p.wr;
+  if (r_edge >= 0) {
+    const int64_t first_q = (int64_t)k0 - (Sk - Sq) - r_edge;  // first query seeing key k0
+    qt_lo = first_q <= 0 ? 0 : (int)(first_q / BQ < num_qt ? first_q / BQ : num_qt);
+    const int64_t q_full = (int64_t)k0 + BK - 1 - (Sk - Sq) - r_edge;  // from here all keys
+    qt_mask = q_full <= 0 ? 0 : (int)((q_full + BQ - 1) / BQ < num_qt ? (q_full + BQ - 1) / BQ : num_qt);
   }
-  const int per_head = num_qt - qt_lo;
+  if (WIN && p.wl >= 0) {
+    const int64_t last_q = (int64_t)k0 + BK - 1 - (Sk - Sq) + p.wl;  // last query seeing a key
+    qt_hi = last_q < 0 ? 0 : (int)(last_q / BQ + 1 < num_qt ? last_q / BQ + 1 : num_qt);
+    const int64_t qa = (int64_t)k0 - (Sk - Sq) + p.wl + 1;  // from here key k0 is left out
+    qt_lmask = qa <= 0 ? 0 : (int)(qa / BQ < num_qt ? qa / BQ : num_qt);
+  }
+  const int per_head = qt_hi > qt_lo ? qt_hi - qt_lo : 0;
   const int items = per_head * p.G;
 
   const int64_t kv_stride = (int64_t)p.Hkv * D;
@@ -473,7 +541,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
       __syncthreads();  // tile it in LDS; phase 2 of tile it-1 done everywhere
       if (it + 1 < items) issue(it + 1);
       const int qt = qt_lo + it % per_head;
-      const bool masked = CAUSAL && qt < qt_mask;
+      const bool masked = (r_edge >= 0 && qt < qt_mask) || (WIN && qt >= qt_lmask);
+      // ALiBi slope of this item's query head in base-2 units
+      const float slope2 =
+          ALIBI ? p.alibi[(int64_t)b * p.alibi_bstride + hk * p.G + it / per_head] * kLog2e : 0.f;
 
       // ---- phase 1: S, dP of (qb, kb); P, dS -> LDS.  Lane (key n, H) holds queries
       // 32 qb + 8H + {0..7} (elements 0..7) and + 16 (elements 8..15).
@@ -485,15 +556,28 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
       for (int w = 0; w < 4; ++w) {  // elements 4w .. 4w+3: queries 16(w/2) + 4(w%2) + ..
         const u32x4 l2 = lds_b128(lds0 + L2_OFF + srow + 4 * (16 * (w >> 1) + 4 * (w & 1)));
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          pr[4 * w + x] = fast_exp2(__builtin_fmaf(sacc[4 * w + x], c2, -__uint_as_float(l2[x])));
+        for (int x = 0; x < 4; ++x) {
+          float y = __builtin_fmaf(sacc[4 * w + x], c2, -__uint_as_float(l2[x]));
+          if constexpr (ALIBI) {  // query qt BQ + 32 qb + 8 H + perm_row(e)
+            const int e = 4 * w + x;
+            const int diag = qt * BQ + 32 * qb + 8 * H + perm_row(e) + Sk - Sq;
+            y = __builtin_fmaf(-slope2, __builtin_fabsf((float)(diag - key)), y);
+          }
+          pr[4 * w + x] = fast_exp2(y);
+        }
       }
       if (masked) {
-        // key <= q + Sk - Sq  <=>  query offset in the tile >= key - (Sk - Sq) - q0
-        const int need = key - (Sk - Sq) - qt * BQ - 8 * H - 32 * qb;
+        // key <= q + Sk - Sq + r  <=>  query offset in the tile >= key - (Sk - Sq) - r - q0;
+        // key >= q + Sk - Sq - wl  <=>  query offset <= key - (Sk - Sq) + wl - q0
+        const int64_t base = (int64_t)key - (Sk - Sq) - qt * BQ - 8 * H - 32 * qb;
+        // element offsets lie in [0, 23]: bounds clamped to [-1, 32] compare as int
+        const int64_t need = r_edge >= 0 ? base - r_edge : -1;
+        const int64_t lim = WIN && p.wl >= 0 ? base + p.wl : 32;
+        const int need_c = (int)(need < -1 ? -1 : (need > 32 ? 32 : need));
+        const int lim_c = (int)(lim < -1 ? -1 : (lim > 32 ? 32 : lim));
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (perm_row(e) < need) pr[e] = 0.f;
+          if (perm_row(e) < need_c || perm_row(e) > lim_c) pr[e] = 0.f;
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half)

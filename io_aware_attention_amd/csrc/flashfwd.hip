@@ -157,6 +157,30 @@ void set_variant(P& p, const Variant& v, float scale) {
   p.cap2 = v.softcap * ff::kLog2e;
 }
 
+// dQ first: its prologue writes each row's D and base-2 LSE into ws, which the dK/dV
+// kernel reads.  var: 0, or the window with or without ALiBi (no soft cap).
+template <int D, bool CAUSAL, int VAR>
+void launch_bwd_var(dim3 g_dq, dim3 g_dkdv, hipStream_t s, const ff::BwdParams& p) {
+  hipLaunchKernelGGL((ff::attn_bwd_dq<D, CAUSAL, VAR>), g_dq, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((ff::attn_bwd_dkdv<D, CAUSAL, VAR>), g_dkdv, dim3(512), 0, s, p);
+}
+
+template <int D>
+void launch_bwd(bool causal, int var, dim3 g_dq, dim3 g_dkdv, hipStream_t s,
+                const ff::BwdParams& p) {
+  using namespace ff;
+  constexpr int W = kVarWindow, WA = kVarWindow | kVarAlibi;
+  if (causal) {
+    if (var == 0) launch_bwd_var<D, true, 0>(g_dq, g_dkdv, s, p);
+    else if (var == W) launch_bwd_var<D, true, W>(g_dq, g_dkdv, s, p);
+    else launch_bwd_var<D, true, WA>(g_dq, g_dkdv, s, p);
+  } else {
+    if (var == 0) launch_bwd_var<D, false, 0>(g_dq, g_dkdv, s, p);
+    else if (var == W) launch_bwd_var<D, false, W>(g_dq, g_dkdv, s, p);
+    else launch_bwd_var<D, false, WA>(g_dq, g_dkdv, s, p);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -185,12 +209,19 @@ long long attn_bwd_workspace_floats(int B, int Sq, int Hq) {
   return 2LL * B * Hq * cdiv(Sq, 64) * 64;
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
-             const void* dout, float* dq, float* dk, float* dv, float* ws, int B, int Sq, int Sk,
-             int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                const void* dout, float* dq, float* dk, float* dv, float* ws, int B, int Sq,
+                int Sk, int Hq, int Hkv, int d, int causal, int window_left, int window_right,
+                const float* alibi_slopes, int alibi_batch_stride, float softcap, float scale,
+                void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !ws) return FF_ERR_NULL;
   int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
   if (st) return st;
+  Variant var;
+  if ((st = check_variant(window_left, window_right, alibi_slopes, alibi_batch_stride, softcap,
+                          Hq, &var)))
+    return st;
+  if (var.softcap > 0.f) return FF_ERR_OPTION;  // the backward takes no soft cap
   const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, ws};
   for (const void* x : ptrs)
     if (!aligned16(x)) return FF_ERR_ALIGN;
@@ -203,9 +234,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
   if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 4))) return st;
   const int64_t in_b[3] = {qf32, (int64_t)B * Hq * Sq * 4, (int64_t)B * Sq * Hq * d * 2};
   const void* ins[3] = {o, lse, dout};
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 3; ++j)
       if (overlaps(outs[i], ob[i], ins[j], in_b[j])) return FF_ERR_ALIAS;
+    if (var.alibi && overlaps(outs[i], ob[i], var.alibi, alibi_bytes(var, B, Hq)))
+      return FF_ERR_ALIAS;
+  }
 
   ff::BwdParams p;
   p.q = (const uint16_t*)q;
@@ -232,30 +266,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const float* o, const 
     return FF_ERR_SHAPE;
   p.scale = scale;
   p.scale_log2 = scale * ff::kLog2e;
+  p.wl = var.wl;
+  p.wr = var.wr;
+  p.alibi = var.alibi;
+  p.alibi_bstride = var.alibi_bstride;
   hipStream_t s = (hipStream_t)stream;
-  // dQ first: its prologue writes each row's D and base-2 LSE into ws, which the dK/dV
-  // kernel reads
-  const dim3 block(256);
   const dim3 g_dq((unsigned)((int64_t)p.num_m * B * Hq));
-  const dim3 g_dkdv((unsigned)((int64_t)p.num_n * B * Hkv)), block_dkdv(512);
-  if (d == 128) {
-    if (causal) {
-      hipLaunchKernelGGL((ff::attn_bwd_dq<128, true>), g_dq, block, 0, s, p);
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, true>), g_dkdv, block_dkdv, 0, s, p);
-    } else {
-      hipLaunchKernelGGL((ff::attn_bwd_dq<128, false>), g_dq, block, 0, s, p);
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<128, false>), g_dkdv, block_dkdv, 0, s, p);
-    }
-  } else {
-    if (causal) {
-      hipLaunchKernelGGL((ff::attn_bwd_dq<64, true>), g_dq, block, 0, s, p);
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, true>), g_dkdv, block_dkdv, 0, s, p);
-    } else {
-      hipLaunchKernelGGL((ff::attn_bwd_dq<64, false>), g_dq, block, 0, s, p);
-      hipLaunchKernelGGL((ff::attn_bwd_dkdv<64, false>), g_dkdv, block_dkdv, 0, s, p);
-    }
-  }
+  const dim3 g_dkdv((unsigned)((int64_t)p.num_n * B * Hkv));
+  if (d == 128) launch_bwd<128>(causal != 0, var.var, g_dq, g_dkdv, s, p);
+  else launch_bwd<64>(causal != 0, var.var, g_dq, g_dkdv, s, p);
   return launch_status();
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const void* dout, float* dq, float* dk, float* dv, float* ws, int B, int Sq, int Sk,
+             int Hq, int Hkv, int d, int causal, float scale, void* stream) {
+  return attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causal, -1,
+                     -1, nullptr, 0, 0.f, scale, stream);
 }
 
 }  // extern "C"

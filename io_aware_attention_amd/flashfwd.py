@@ -22,7 +22,7 @@ EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_splitkv_num_split
            "attn_splits_efficiency_rule", "attn_fwd_splitkv", "attn_splitkv_combine",
            "attn_fwd_kvcache", "attn_fwd_kvcache_ex", "attn_kvcache_append",
            "attn_quantize_fp8", "attn_fwd_fp8", "attn_bwd_workspace_floats", "attn_bwd",
-           "attn_status_string")
+           "attn_bwd_ex", "attn_status_string")
 
 
 class FlashFwdError(RuntimeError):
@@ -73,6 +73,7 @@ def load(path=LIB_PATH):
     lib.attn_fwd_fp8.argtypes = [P] * 8 + [I] * 7 + [F, P]
     lib.attn_bwd_workspace_floats.argtypes = [I, I, I]
     lib.attn_bwd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, P]
+    lib.attn_bwd_ex.argtypes = [P] * 10 + [I] * 9 + [P, I, F, F, P]
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -217,6 +218,16 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causa
                            float(scale), _stream(stream)), "attn_bwd")
 
 
+def attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causal,
+                window_left, window_right, alibi_slopes, alibi_batch_stride, softcap, scale,
+                stream=None):
+    _check(load().attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), B, Sq, Sk, Hq, Hkv, d,
+                              int(bool(causal)), int(window_left), int(window_right),
+                              _ptr(alibi_slopes), int(alibi_batch_stride), float(softcap),
+                              float(scale), _stream(stream)), "attn_bwd_ex")
+
+
 # ---------------------------------------------------------------------------
 # torch conveniences: allocate outputs with torch, then call the entry points above.
 
@@ -357,9 +368,11 @@ def forward_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal, scale, stream=Non
     return o, lse
 
 
-def backward(q, k, v, o, lse, dout, causal, scale, stream=None):
+def backward(q, k, v, o, lse, dout, causal, scale, stream=None, window=(-1, -1),
+             alibi_slopes=None):
     """dq [B,Sq,Hq,d], dk and dv [B,Sk,Hkv,d] fp32 from bf16 q, k, v, dout and the fp32 o, lse
-    of the forward; the workspace is allocated here."""
+    of the forward (with the same window and ALiBi slopes); the workspace is allocated
+    here."""
     import torch
     B, Sq, Hq, d = q.shape
     _, Sk, Hkv, _ = k.shape
@@ -367,5 +380,11 @@ def backward(q, k, v, o, lse, dout, causal, scale, stream=None):
     dk = torch.empty((B, Sk, Hkv, d), dtype=torch.float32, device=q.device)
     dv = torch.empty((B, Sk, Hkv, d), dtype=torch.float32, device=q.device)
     ws = torch.empty(attn_bwd_workspace_floats(B, Sq, Hq), dtype=torch.float32, device=q.device)
-    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causal, scale, stream)
+    if tuple(window) == (-1, -1) and alibi_slopes is None:
+        attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causal, scale,
+                 stream)
+    else:
+        attn_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d, causal,
+                    window[0], window[1], alibi_slopes, _alibi_stride(alibi_slopes, Hq), 0.0,
+                    scale, stream)
     return dq, dk, dv

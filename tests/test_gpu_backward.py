@@ -148,3 +148,62 @@ def test_backward_full_size_causal_prefill(oracle):
     err = np.abs(got - want)
     say(f"  sum_j dV_j vs sum_i dO_i: worst err / (2^-7 sum|dO|) = {(err / (2 ** -7 * absum)).max():.3f}")
     assert (err <= 2.0 ** -7 * absum).all()
+
+
+VARIANT_CASES = [  # (B, Sq, Sk, Hq, Hkv, d, causal, window, alibi: None | "head" | "batch")
+    (1, 300, 300, 4, 2, 128, False, (70, 20), None),     # two-sided window
+    (2, 200, 333, 2, 1, 64, True, (100, 0), None),       # causal window, Sq < Sk
+    (1, 333, 200, 2, 2, 128, True, (50, -1), None),      # Sq > Sk: rows with no key
+    (1, 257, 257, 4, 1, 64, False, (-1, 40), "head"),    # right limit only, ALiBi per head
+    (2, 190, 190, 2, 2, 128, True, (130, 0), "batch"),   # ALiBi per (batch, head)
+    (1, 400, 400, 2, 1, 128, False, (1, 1), None),       # three keys per query
+]
+
+
+def variant_ids(c):
+    B, Sq, Sk, Hq, Hkv, d, causal, win, al = c
+    return (f"B{B}_Sq{Sq}_Sk{Sk}_Hq{Hq}_Hkv{Hkv}_d{d}_{'causal' if causal else 'full'}"
+            f"_w{win[0]}_{win[1]}_{al}")
+
+
+@pytest.mark.parametrize("case", VARIANT_CASES, ids=variant_ids)
+def test_backward_variants_match_oracle(oracle, case):
+    import torch
+    from io_aware_attention_amd import flashfwd as ff
+    B, Sq, Sk, Hq, Hkv, d, causal, window, al = case
+    say(f"backward variants {variant_ids(case)}")
+    q, k, v = make_inputs(B, Sq, Sk, Hq, Hkv, d, seed=41)
+    dout = synth.normal_bf16(41, 3, (B, Sq, Hq, d))
+    scale = synth.f32(1.0 / np.sqrt(d))
+    slopes = None
+    if al == "head":
+        slopes = np.array([2.0 ** -(i + 1) for i in range(Hq)], np.float32)
+    elif al == "batch":
+        slopes = np.array([[2.0 ** -(i + 1 + b) for i in range(Hq)] for b in range(B)], np.float32)
+    o, lse = oracle.fwd(q, k, v, causal, scale, window=window, alibi=slopes)
+    dq, dk, dv, _, (bq, bk, bv) = oracle.bwd(q, k, v, dout, causal, scale, window=window,
+                                             alibi=slopes)
+    o_d = torch.from_numpy(np.ascontiguousarray(o, dtype=np.float32)).to("cuda:0")
+    lse_d = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).to("cuda:0")
+    sl_d = None if slopes is None else torch.from_numpy(slopes).to("cuda:0")
+    gq, gk, gv = ff.backward(to_dev(q), to_dev(k), to_dev(v), o_d, lse_d, to_dev(dout), causal,
+                             scale, window=window, alibi_slopes=sl_d)
+    torch.cuda.synchronize()
+    check_grad(host(gq), dq, bq, "dQ")
+    check_grad(host(gk), dk, bk, "dK")
+    check_grad(host(gv), dv, bv, "dV")
+
+
+def test_backward_rejects_softcap():
+    import torch
+    from io_aware_attention_amd import flashfwd as ff
+    B, S, H, d = 1, 64, 1, 64
+    x = torch.zeros((B, S, H, d), dtype=torch.bfloat16, device="cuda:0")
+    o = torch.zeros((B, S, H, d), dtype=torch.float32, device="cuda:0")
+    lse = torch.zeros((B, H, S), dtype=torch.float32, device="cuda:0")
+    g = [torch.empty((B, S, H, d), dtype=torch.float32, device="cuda:0") for _ in range(3)]
+    ws = torch.empty(ff.attn_bwd_workspace_floats(B, S, H), dtype=torch.float32, device="cuda:0")
+    with pytest.raises(ff.FlashFwdError) as e:
+        ff.attn_bwd_ex(x, x, x, o, lse, x, *g, ws, B, S, S, H, H, d, False, -1, -1, None, 0,
+                       5.0, 0.125)
+    assert e.value.status == 10  # FF_ERR_OPTION
