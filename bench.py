@@ -42,6 +42,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "causal_prefill"
 DECODE = "gqa_decode"
 BACKWARD = "causal_prefill_bwd"   # attn_bwd over causal_prefill's inputs
+# backward workloads and the forward workloads whose inputs (and options) they take
+BWD_SOURCES = {BACKWARD: "causal_prefill", "sliding_window_gqa_bwd": "sliding_window_gqa"}
 PROFILES = os.path.join(ROOT, "profiles")
 # The device sources each kernel is compiled from (its template code and the shared
 # building blocks); a change to any of them makes its committed counter summary stale.
@@ -271,17 +273,19 @@ def run_varlen(torch, ff, name, steps, warmup):
                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}}
 
 
-def run_backward(torch, ff, steps, warmup):
-    """attn_bwd on causal_prefill's inputs: dO is tensor 3 of the workload's seed, O and LSE
-    come from attn_fwd.  A step is the two backward kernels (dQ, which also computes each
-    row's D and base-2 LSE, then dK/dV)."""
-    w = synth.WORKLOADS[HEADLINE]
+def run_backward(torch, ff, name, steps, warmup):
+    """The backward over a forward workload's inputs (causal_prefill, or sliding_window_gqa
+    through attn_bwd_ex with its window): dO is tensor 3 of the workload's seed, O and LSE
+    come from the forward with the same options.  A step is the two backward kernels (dQ,
+    which also computes each row's D and base-2 LSE, then dK/dV)."""
+    w = synth.WORKLOADS[BWD_SOURCES[name]]
     q, k, v = synth.make_qkv(w)
     dout = synth.normal_bf16(w["seed"], 3, q.shape)
     qd, kd, vd, dod = (to_dev(torch, x) for x in (q, k, v, dout))
     del q, k, v, dout
     B, Sq, Sk, Hq, Hkv, d = (w[x] for x in ("B", "Sq", "Sk", "Hq", "Hkv", "d"))
-    o, lse = ff.forward(qd, kd, vd, w["causal"], w["scale"])
+    win = window_of(w)
+    o, lse = ff.forward(qd, kd, vd, w["causal"], w["scale"], window=win)
     dq = torch.empty((B, Sq, Hq, d), dtype=torch.float32, device="cuda:0")
     dk = torch.empty((B, Sk, Hkv, d), dtype=torch.float32, device="cuda:0")
     dv = torch.empty((B, Sk, Hkv, d), dtype=torch.float32, device="cuda:0")
@@ -290,8 +294,12 @@ def run_backward(torch, ff, steps, warmup):
     stream = torch.cuda.current_stream()
 
     def step():
-        ff.attn_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d,
-                    w["causal"], w["scale"], stream)
+        if win == (-1, -1):
+            ff.attn_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d,
+                        w["causal"], w["scale"], stream)
+        else:
+            ff.attn_bwd_ex(qd, kd, vd, o, lse, dod, dq, dk, dv, ws, B, Sq, Sk, Hq, Hkv, d,
+                           w["causal"], win[0], win[1], None, 0, 0.0, w["scale"], stream)
 
     for _ in range(warmup):
         step()
@@ -305,9 +313,9 @@ def run_backward(torch, ff, steps, warmup):
     assert all(torch.isfinite(x).all().item() for x in (dq, dk, dv)), "non-finite gradient"
     flops = 2.5 * prefill_flops(w)   # 10*d per visible pair: S, dP, dV, dQ, dK
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] {BACKWARD}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s "
+    log(f"[bench] {name}: {ms:.4f} ms/step, {tflops:.1f} TFLOP/s "
         f"({100 * tflops / PEAK_BF16_TFLOPS:.1f}% of dense bf16 peak)")
-    return {"workload": BACKWARD, "metric": "TFLOP/s", "value": round(tflops, 2),
+    return {"workload": name, "metric": "TFLOP/s", "value": round(tflops, 2),
             "ms_per_step": round(ms, 4), "kernel": "attn_bwd_dkdv",
             "kernels": ["attn_bwd_dq", "attn_bwd_dkdv"],
             "algorithmic_flop_per_launch": flops,
@@ -460,7 +468,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workloads", default="all",
-                    help="comma list of " + ",".join(list(synth.WORKLOADS) + [BACKWARD]) + " (default: all)")
+                    help="comma list of " + ",".join(list(synth.WORKLOADS) + list(BWD_SOURCES)) + " (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -487,7 +495,7 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": args.steps}), flush=True)
         return
 
-    names = list(synth.WORKLOADS) + [BACKWARD] if args.workloads == "all" else \
+    names = list(synth.WORKLOADS) + list(BWD_SOURCES) if args.workloads == "all" else \
         args.workloads.split(",")
     results = {}
     headline_inputs = None
@@ -495,8 +503,8 @@ def main():
         log(f"[bench] running {name} ...")
         if name in (DECODE, "paged_decode"):
             results[name] = run_decode(torch, ff, name, args.steps, args.warmup)
-        elif name == BACKWARD:
-            results[name] = run_backward(torch, ff, args.steps, args.warmup)
+        elif name in BWD_SOURCES:
+            results[name] = run_backward(torch, ff, name, args.steps, args.warmup)
         elif "total" in synth.WORKLOADS[name]:
             results[name] = run_varlen(torch, ff, name, args.steps, args.warmup)
         elif synth.WORKLOADS[name].get("fp8"):
