@@ -112,12 +112,16 @@ __device__ __forceinline__ i32x4 buffer_desc(const void* base, uint32_t num_reco
 // lds_base + 16 * lane (buffer_load_dwordx4 ... lds; lds_base is wave-uniform).
 // Written as inline assembly: the compiler then neither tracks nor orders other LDS
 // reads behind these loads, so the caller must wait (vmcnt) and synchronise before
-// reading what they wrote.
+// reading what they wrote.  The LDS address travels in M0, which the "{m0}" operand has
+// the compiler load itself (so no live value of its own sits in M0 across the
+// statement).  On this GPU generation an LDS DMA that reads M0 needs one wait state
+// after the scalar write of M0, and the compiler does not know what the statement
+// holds: the s_nop provides it.
 __device__ __forceinline__ void buffer_load_lds16(i32x4 desc, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(desc), "s"(lds_base)
-               : "memory", "m0");
+               : "v"(voff), "s"(desc), "{m0}"(lds_base)
+               : "memory");
 }
 
 // All of this wave's vector-memory loads (including loads into LDS) have completed.  The

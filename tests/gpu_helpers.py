@@ -53,6 +53,25 @@ def sample_rows(B, Sq, Hq, n, seed, boundaries=(127, 128, 255, 256)):
     return sorted(rows)
 
 
+def tile_edge_rows(B, Sq, Hq, seed, bm=128, per_tile=2):
+    """(b, h, i) triples covering every (batch, head, bm-row query tile): its first and
+    last row (per_tile=2), or one seeded row inside it (per_tile=1).  bm is the prefill
+    kernel's query-tile height, so every workgroup of a launch is checked."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for b in range(B):
+        for h in range(Hq):
+            for m0 in range(0, Sq, bm):
+                last = min(m0 + bm, Sq) - 1
+                if per_tile == 2:
+                    rows.append((b, h, m0))
+                    if last != m0:
+                        rows.append((b, h, last))
+                else:
+                    rows.append((b, h, int(rng.integers(m0, last + 1))))
+    return rows
+
+
 def make_inputs(B, Sq, Sk, Hq, Hkv, d, seed, mult=1.0):
     q = synth.normal_bf16(seed, 0, (B, Sq, Hq, d), mult)
     k = synth.normal_bf16(seed, 1, (B, Sk, Hkv, d), mult)

@@ -157,6 +157,8 @@ VARIANT_CASES = [  # (B, Sq, Sk, Hq, Hkv, d, causal, window, alibi: None | "head
     (1, 257, 257, 4, 1, 64, False, (-1, 40), "head"),    # right limit only, ALiBi per head
     (2, 190, 190, 2, 2, 128, True, (130, 0), "batch"),   # ALiBi per (batch, head)
     (1, 400, 400, 2, 1, 128, False, (1, 1), None),       # three keys per query
+    (1, 64, 400, 2, 1, 128, False, (10, 0), None),       # keys 0..325 seen by no query
+    (1, 400, 64, 2, 1, 64, True, (5, 0), None),          # Sq >> Sk: few query tiles per key block
 ]
 
 
@@ -192,6 +194,11 @@ def test_backward_variants_match_oracle(oracle, case):
     check_grad(host(gq), dq, bq, "dQ")
     check_grad(host(gk), dk, bk, "dK")
     check_grad(host(gv), dv, bv, "dV")
+    # keys that no query sees get exactly zero gradients
+    unseen = ~np.any(bk != 0, axis=(0, 2, 3)) if bk.ndim == 4 else None
+    if unseen is not None and unseen.any():
+        say(f"  {int(unseen.sum())} keys seen by no query: dK, dV must be exact zeros")
+        assert not host(gk)[:, unseen].any() and not host(gv)[:, unseen].any()
 
 
 def test_backward_rejects_softcap():

@@ -21,7 +21,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import LSE_TOL, host, make_inputs, sample_rows, say, to_dev
+from gpu_helpers import LSE_TOL, host, make_inputs, say, tile_edge_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -165,9 +165,10 @@ def test_fp8_attention(ff, oracle, case):
     check_fp8(host(o), host(lse), o_ref, lse_ref, tol, str(case))
 
 
-def test_fp8_full_size_sampled(ff, oracle):
-    # causal_prefill's tensors quantized on the GPU; sampled rows against the oracle on the
-    # dequantized tensors (the FP8 attention's definition)
+def test_fp8_full_size_every_tile(ff, oracle):
+    # causal_prefill's tensors quantized on the GPU; one seeded row of every (batch, head,
+    # 128-row query tile) against the oracle on the dequantized tensors (the FP8
+    # attention's definition)
     import torch
     w = synth.WORKLOADS["causal_prefill"]
     say(f"full-size fp8 on causal_prefill: {w}")
@@ -181,8 +182,8 @@ def test_fp8_full_size_sampled(ff, oracle):
     q8, k8, v8 = (x.cpu().numpy() for x in (q8, k8, v8))
     qs, ks, vs = (x.cpu().numpy() for x in (qs, ks, vs))
     qd, kd, vd = (oracle.dequantize_fp8(c, s) for c, s in ((q8, qs), (k8, ks), (v8, vs)))
-    rows = sample_rows(w["B"], w["Sq"], w["Hq"], 24, seed=41,
-                       boundaries=(63, 64, 127, 128, 4095))
+    rows = tile_edge_rows(w["B"], w["Sq"], w["Hq"], seed=41, per_tile=1)
+    say(f"  comparing {len(rows)} rows (one in every query tile)")
     o_ref, lse_ref = oracle.rows(qd, kd, vd, True, w["scale"], rows)
     idx = torch.tensor(rows, dtype=torch.long)
     o_s = host(o_d[idx[:, 0], idx[:, 2], idx[:, 1]])

@@ -1,15 +1,16 @@
 """attn_fwd (the fused prefill kernel) against the fp64 CPU oracle, element by element.
 
 Small shapes spanning several query and key tiles with ragged tails are compared in full;
-the full-size workloads are compared on sampled rows (the oracle computes them one by
-one) plus properties that hold at any size.  Calls go through the C ABI."""
+the full-size workloads are compared on the first and last row of every (batch, head,
+128-row query tile), so every workgroup of the launch is checked (the oracle computes the
+rows one by one), plus properties that hold at any size.  Calls go through the C ABI."""
 import math
 
 import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import check_outputs, host, make_inputs, sample_rows, say, to_dev
+from gpu_helpers import check_outputs, host, make_inputs, say, tile_edge_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -81,7 +82,7 @@ def test_tiny_mha_workload_full(ff, oracle):
 
 @pytest.mark.parametrize("name", ["causal_prefill", "ragged_noncausal", "ragged_causal",
                                   "long_causal_gqa"])
-def test_prefill_full_size_sampled(ff, oracle, name):
+def test_prefill_full_size_every_tile(ff, oracle, name):
     import torch
     w = synth.WORKLOADS[name]
     say(f"full-size workload {name}: {w}")
@@ -92,8 +93,8 @@ def test_prefill_full_size_sampled(ff, oracle, name):
     assert torch.isfinite(o_d).all().item() and torch.isfinite(lse_d).all().item()
     vmax = float(np.abs(synth.bf16_bits_to_f32(v)).max())
     assert o_d.abs().max().item() <= vmax + 2e-2   # O is a convex combination of V rows
-    rows = sample_rows(w["B"], w["Sq"], w["Hq"], 96, seed=len(name),
-                       boundaries=(63, 64, 127, 128, 129, 4095, 4096, w["Sq"] - 2))
+    rows = tile_edge_rows(w["B"], w["Sq"], w["Hq"], seed=len(name))
+    say(f"  comparing {len(rows)} rows (first and last of every query tile)")
     o_ref, lse_ref = oracle.rows(q, k, v, w["causal"], w["scale"], rows)
     idx = torch.tensor(rows, dtype=torch.long)
     o_s = o_d[idx[:, 0], idx[:, 2], idx[:, 1]]

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import check_outputs, host, make_inputs, sample_rows, say, to_dev
+from gpu_helpers import check_outputs, host, make_inputs, say, tile_edge_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -129,7 +129,7 @@ def test_softcap_closed_form_on_gpu(ff, d):
     assert abs(lse[0, 0, 0] - math.log(1 + e)) < 1e-3
 
 
-def test_sliding_window_full_size_sampled(ff, oracle):
+def test_sliding_window_full_size_every_tile(ff, oracle):
     import torch
     w = synth.WORKLOADS["sliding_window_gqa"]
     say(f"full-size workload sliding_window_gqa: {w}")
@@ -139,8 +139,8 @@ def test_sliding_window_full_size_sampled(ff, oracle):
                             window=win)
     torch.cuda.synchronize()
     assert torch.isfinite(o_d).all().item() and torch.isfinite(lse_d).all().item()
-    rows = sample_rows(w["B"], w["Sq"], w["Hq"], 64, seed=31,
-                       boundaries=(63, 64, 4095, 4096, 4097, 8191, w["Sq"] - 1))
+    rows = tile_edge_rows(w["B"], w["Sq"], w["Hq"], seed=31)
+    say(f"  comparing {len(rows)} rows (first and last of every query tile)")
     o_ref, lse_ref = oracle.rows(q, k, v, w["causal"], w["scale"], rows, window=win)
     idx = torch.tensor(rows, dtype=torch.long)
     check_outputs(host(o_d[idx[:, 0], idx[:, 2], idx[:, 1]]),
