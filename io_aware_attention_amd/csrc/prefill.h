@@ -413,6 +413,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
   }
   if (t >= n_mask_lo || t < n_bot) mask(S[0], t);
   float mx = rowmax(S[0]);
+  // Every wave has read K of the first tile before the first step refills its buffer.
+  __syncthreads();
 
   // One step (parity P): softmax + PV of tile t; QK^T, mask and row max of tile t-1
   // if HAS_NEXT.
