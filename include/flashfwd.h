@@ -56,7 +56,8 @@ typedef enum {
   FF_ERR_SCALE = 7,    /* scale not finite or not > 0 */
   FF_ERR_HIP = 8,      /* the HIP runtime reported an error (device query or launch) */
   FF_ERR_ALIAS = 9,    /* an output overlaps an input */
-  FF_ERR_OPTION = 10   /* a mask/bias option out of range (the _ex entry points) */
+  FF_ERR_OPTION = 10,  /* a mask/bias option out of range (the _ex entry points) */
+  FF_ERR_SCRATCH = 11  /* attn_fwd_splitkv_noalloc: the partials exceed the library's buffer */
 } ff_status;
 
 #define FF_MAX_SPLITS 128
@@ -152,6 +153,23 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v,
  * gets O = 0, LSE = -inf.  Writes o [B,Sq,Hq,d] and lse [B,Hq,Sq]. */
 int attn_splitkv_combine(const float* o_accum, const float* lse_accum, float* o, float* lse,
                          int B, int Sq, int Hq, int d, int num_splits, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): attn_fwd_splitkv followed, for
+ * num_splits > 1, by attn_splitkv_combine, with the split partials kept in a device
+ * buffer the library owns instead of caller buffers.  The buffer is a static array of
+ * FF_NOALLOC_SCRATCH_FLOATS floats (16 MiB), one per GPU, held until the process ends;
+ * the call allocates nothing and frees nothing.  It needs num_splits * B * Hq * Sq *
+ * (d + 1) floats of it (num_splits > 1; none for one split) and returns FF_ERR_SCRATCH
+ * when that is larger.  Every call on a GPU uses that GPU's one buffer: calls that
+ * overlap in time on one GPU (different streams, or other threads) race on it, so
+ * callers serialise them (one stream, say).  Arguments, layouts, outputs and the other
+ * errors as attn_fwd_splitkv and attn_splitkv_combine; all checks are made before
+ * anything is enqueued.  FF_ERR_HIP if the buffer's device address cannot be obtained. */
+#define FF_NOALLOC_SCRATCH_FLOATS (4 << 20)
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                             int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
+                             float scale, int num_splits, void* stream);
 
 /* Split-KV forward against a key/value cache (the decode path of "03 forward CUDA
  * kernel" section 8, which sends cached attention through the split-KV kernel; "flash

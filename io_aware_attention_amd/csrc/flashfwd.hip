@@ -200,6 +200,8 @@ const char* attn_status_string(int status) {
     case FF_ERR_OPTION:
       return "invalid mask/bias option (window < -1, softcap < 0 or not finite, "
              "or ALiBi batch stride not 0 or Hq)";
+    case FF_ERR_SCRATCH:
+      return "the split partials need more than FF_NOALLOC_SCRATCH_FLOATS floats";
     default: return "unknown status";
   }
 }
@@ -731,6 +733,63 @@ int attn_splitkv_combine(const float* o_accum, const float* lse_accum, float* o,
   if (d == 128) hipLaunchKernelGGL(ff::attn_splitkv_combine<128>, grid, block, 0, s, p);
   else hipLaunchKernelGGL(ff::attn_splitkv_combine<64>, grid, block, 0, s, p);
   return launch_status();
+}
+
+}  // extern "C"
+
+namespace {
+
+// The split partials of attn_fwd_splitkv_noalloc.  Each GPU the library runs on holds its
+// own copy until the process ends.  On the host, `scratch` only names the array: its
+// device address (per GPU) comes from hipGetSymbolAddress and is kept in g_scratch.
+static __device__ __align__(256) float scratch[FF_NOALLOC_SCRATCH_FLOATS];
+std::atomic<float*> g_scratch[64];
+
+// The current device's address of `scratch`, looked up on the first call on that device.
+int scratch_address(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FF_ERR_HIP;
+  float* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return FF_ERR_HIP;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return FF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                             int B, int Sq, int Sk, int Hq, int Hkv, int d, int causal,
+                             float scale, int num_splits, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FF_ERR_NULL;
+  if (num_splits < 1 || num_splits > FF_MAX_SPLITS) return FF_ERR_SPLITS;
+  int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
+  if (st) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FF_ERR_ALIGN;
+  if ((st = check_scale(scale))) return st;
+  const int64_t rows = (int64_t)B * Hq * Sq;
+  const void* outs[2] = {o, lse};
+  const int64_t ob[2] = {rows * d * 4, rows * 4};
+  if ((st = check_io(q, k, v, B, Sq, Sk, Hq, Hkv, d, outs, ob, 2))) return st;
+  if (num_splits == 1)
+    return attn_fwd_splitkv(q, k, v, nullptr, nullptr, o, lse, B, Sq, Sk, Hq, Hkv, d, causal,
+                            scale, 1, stream);
+  if ((int64_t)num_splits * rows * (d + 1) > FF_NOALLOC_SCRATCH_FLOATS) return FF_ERR_SCRATCH;
+  float* base = nullptr;
+  if ((st = scratch_address(&base))) return st;
+  // partial O first, then the partial LSEs (16-byte aligned: d is a multiple of 4)
+  float* o_accum = base;
+  float* lse_accum = base + (int64_t)num_splits * rows * d;
+  if ((st = attn_fwd_splitkv(q, k, v, o_accum, lse_accum, nullptr, nullptr, B, Sq, Sk, Hq, Hkv,
+                             d, causal, scale, num_splits, stream)))
+    return st;
+  return attn_splitkv_combine(o_accum, lse_accum, o, lse, B, Sq, Hq, d, num_splits, stream);
 }
 
 }  // extern "C"

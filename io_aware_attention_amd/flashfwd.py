@@ -17,12 +17,13 @@ FF_MAX_SPLITS = 128
 FF_SPLIT_BLOCK_N = 128
 STATUS_NAMES = {0: "FF_OK", 1: "FF_ERR_NULL", 2: "FF_ERR_SHAPE", 3: "FF_ERR_HEADDIM",
                 4: "FF_ERR_GQA", 5: "FF_ERR_ALIGN", 6: "FF_ERR_SPLITS", 7: "FF_ERR_SCALE",
-                8: "FF_ERR_HIP", 9: "FF_ERR_ALIAS", 10: "FF_ERR_OPTION"}
+                8: "FF_ERR_HIP", 9: "FF_ERR_ALIAS", 10: "FF_ERR_OPTION", 11: "FF_ERR_SCRATCH"}
+FF_NOALLOC_SCRATCH_FLOATS = 4 << 20
 EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_varlen", "attn_splitkv_num_splits",
            "attn_splits_efficiency_rule", "attn_fwd_splitkv", "attn_splitkv_combine",
            "attn_fwd_kvcache", "attn_fwd_kvcache_ex", "attn_kvcache_append",
            "attn_quantize_fp8", "attn_fwd_fp8", "attn_bwd_workspace_floats", "attn_bwd",
-           "attn_bwd_ex", "attn_status_string")
+           "attn_bwd_ex", "attn_fwd_splitkv_noalloc", "attn_status_string")
 
 
 class FlashFwdError(RuntimeError):
@@ -74,6 +75,7 @@ def load(path=LIB_PATH):
     lib.attn_bwd_workspace_floats.argtypes = [I, I, I]
     lib.attn_bwd.argtypes = [P] * 10 + [I, I, I, I, I, I, I, F, P]
     lib.attn_bwd_ex.argtypes = [P] * 10 + [I] * 9 + [P, I, F, F, P]
+    lib.attn_fwd_splitkv_noalloc.argtypes = [P] * 5 + [I] * 7 + [F, I, P]
     lib.attn_status_string.argtypes = [I]
     lib.attn_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -159,6 +161,14 @@ def attn_splitkv_combine(o_accum, lse_accum, o, lse, B, Sq, Hq, d, num_splits, s
     _check(load().attn_splitkv_combine(_ptr(o_accum), _ptr(lse_accum), _ptr(o), _ptr(lse), B,
                                        Sq, Hq, d, int(num_splits), _stream(stream)),
            "attn_splitkv_combine")
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, o, lse, B, Sq, Sk, Hq, Hkv, d, causal, scale,
+                             num_splits, stream=None):
+    _check(load().attn_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Sq,
+                                           Sk, Hq, Hkv, d, int(bool(causal)), float(scale),
+                                           int(num_splits), _stream(stream)),
+           "attn_fwd_splitkv_noalloc")
 
 
 def attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, cache_leftpad, block_table, o_accum,

@@ -63,7 +63,10 @@ int main() {
   expect((int)attn_bwd_workspace_floats(0, 65, 3), -FF_ERR_SHAPE, "workspace shape");
   expect(attn_bwd(Q, K, V, O, L, Q, W, A, A, A, 1, 8, 8, 2, 1, 64, 0, 0.125f, nullptr), FF_ERR_ALIAS, "bwd alias");
   expect(attn_bwd_ex(Q, K, V, O, L, Q, W, A, O, L, 1, 8, 8, 2, 1, 64, 0, -1, -1, nullptr, 0, 2.f, 0.125f, nullptr), FF_ERR_OPTION, "bwd softcap");
-  for (int s = 0; s <= 11; ++s)
+  expect(attn_fwd_splitkv_noalloc(Q, K, V, O, L, 8, 16, 64, 32, 8, 128, 0, 0.1f, 128, nullptr), FF_ERR_SCRATCH, "noalloc size");
+  expect(attn_fwd_splitkv_noalloc(Q, K, V, O, L, 1, 1, 64, 8, 2, 128, 0, 0.1f, 0, nullptr), FF_ERR_SPLITS, "noalloc splits");
+  expect(attn_fwd_splitkv_noalloc(Q, K, V, (float*)K, L, 1, 1, 64, 8, 2, 128, 0, 0.1f, 4, nullptr), FF_ERR_ALIAS, "noalloc alias");
+  for (int s = 0; s <= 12; ++s)
     if (!attn_status_string(s)[0]) expect(0, 1, "status string");
   if (failures) return 1;
   printf("host driver: all checks passed\n");

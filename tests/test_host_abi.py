@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(11):
+    for code in range(12):
         assert ff.status_string(code)
     assert ff.status_string(0) == "ok"
 
@@ -308,3 +308,24 @@ def test_one_hip_runtime_whatever_the_import_order():
             "print(len(libs)); assert len(libs) == 1, libs\n") % ROOT
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+NOALLOC = dict(B=1, Sq=1, Sk=64, Hq=8, Hkv=2, d=128, causal=0, scale=0.1, S=4)
+
+
+def call_noalloc(q=Q, k=K, v=V, o=O, lse=L, **kw):
+    a = dict(NOALLOC, **kw)
+    return ff.load().attn_fwd_splitkv_noalloc(q, k, v, o, lse, a["B"], a["Sq"], a["Sk"], a["Hq"],
+                                              a["Hkv"], a["d"], a["causal"], a["scale"], a["S"],
+                                              None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(o=None), 1), (dict(S=0), 6), (dict(S=129), 6), (dict(d=96), 3), (dict(Hq=6, Hkv=4), 4),
+    (dict(lse=L + 4), 5), (dict(scale=0.0), 7), (dict(o=K), 9),
+    # partials of 128 splits x 8 x 32 x 16 rows x 129 floats exceed the 4 Mi-float buffer
+    (dict(B=8, Hq=32, Hkv=8, Sq=16, S=128), 11),
+    (dict(B=1, Hq=8, Hkv=2, Sq=4096, S=2), 11),
+])
+def test_attn_fwd_splitkv_noalloc_rejects(kw, code):
+    assert call_noalloc(**kw) == code
