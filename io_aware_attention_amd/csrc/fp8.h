@@ -104,6 +104,22 @@ __device__ __forceinline__ void fp8_mfma_drain(f32x16& a, f32x16& b) {
 __device__ __forceinline__ void fp8_mfma_drain(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
   asm volatile(FF_FP8_DRAIN_NOPS : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
+// The same instruction also reads its 32-byte A and B operands later than the compiler
+// assumes: taking the sources as free right after the issue, it may write other values
+// into them at once (a pipelined version of this kernel wrote a row maximum into the
+// probability registers one instruction after the last PV product, and its last 32 dcols
+// came out wrong).  So the operands of the last product of a block are kept live, as
+// inputs of the statement below, through 64 more wait states.
+#define FF_FP8_HOLD_NOPS "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+__device__ __forceinline__ void fp8_mfma_hold(const Frag32& a, const Frag32& b) {
+  asm volatile(FF_FP8_HOLD_NOPS ::"v"(a.lo), "v"(a.hi), "v"(b.lo), "v"(b.hi));
+}
+// The result drain of two accumulators that also keeps the A operand of the last product
+// (its B operand is a Q fragment, never written) live until it ends.
+__device__ __forceinline__ void fp8_mfma_drain_hold(f32x16& a, f32x16& b, const Frag32& s) {
+  asm volatile(FF_FP8_DRAIN_NOPS : "+v"(a), "+v"(b) : "v"(s.lo), "v"(s.hi));
+}
+
 template <int N>
 __device__ __forceinline__ void fp8_mfma_drain(f32x16 (&acc)[N]) {
   static_assert(N == 2 || N == 4, "two or four accumulators");
@@ -129,7 +145,7 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fwd_fp8(Fp8Params p) {
+__global__ __launch_bounds__(256, 3) void attn_fwd_fp8(Fp8Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Fp8Traits<D>;
   constexpr int BM = T::BM, BN = T::BN, ROWB = T::ROWB, CPR = T::CPR, TILE = T::TILE;
@@ -269,11 +285,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8(Fp8Params p) {
     const uint32_t base = kl + kb * 32 * ROWB;
     return Frag32{lds_ld16(base + ka[c][0]), lds_ld16(base + ka[c][1])};
   };
+  // QK^T of the K tile at kl, then the result drain (which also holds the K fragments of
+  // the last two products).
   auto gemm0 = [&](uint32_t kl, f32x16* sc) {
     sc[0] = f32x16{};
     sc[1] = f32x16{};
+    Frag32 kf;
 #pragma unroll
-    for (int i = 0; i < 2 * NC; ++i) sc[i & 1] = mfma32_fp8(kread(kl, i), qf[i >> 1], sc[i & 1]);
+    for (int i = 0; i < 2 * NC; ++i) {
+      kf = kread(kl, i);
+      sc[i & 1] = mfma32_fp8(kf, qf[i >> 1], sc[i & 1]);
+    }
+    fp8_mfma_drain_hold(sc[0], sc[1], kf);
   };
   // Score element e (block e / 16, index e % 16 = 4j + i) of tile t is key
   // t BN + 4H + key_off(e), key_off(e) = 32 (e / 16) + 8 j + i.
@@ -334,7 +357,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8(Fp8Params p) {
 
     f32x16 sc[2];
     gemm0(smem_addr + P * TILE, sc);
-    fp8_mfma_drain(sc);
     if constexpr (MASK) mask(sc, t);
     const float mx = rowmax(sc) * ts.c2;
     const bool raise = mx > m_run + kRescaleSlack;
@@ -366,14 +388,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_fp8(Fp8Params p) {
     l_run += (lsum[0] + lsum[1]) * ts.ir;
 
     const uint32_t vl = smem_addr + (2 + P) * TILE;
+    Frag32 vf;
 #pragma unroll
     for (int db = 0; db < NG1; ++db) {
       const uint32_t a = vl + va[db];
       const u32x2 r0 = ds_read_tr8_b64<0>(a), r1 = ds_read_tr8_b64<16 * ROWB>(a);
       const u32x2 r2 = ds_read_tr8_b64<32 * ROWB>(a), r3 = ds_read_tr8_b64<48 * ROWB>(a);
-      const Frag32 vf = {u32x4{r0[0], r0[1], r1[0], r1[1]}, u32x4{r2[0], r2[1], r3[0], r3[1]}};
+      vf = Frag32{u32x4{r0[0], r0[1], r1[0], r1[1]}, u32x4{r2[0], r2[1], r3[0], r3[1]}};
       oacc[db] = mfma32_fp8(vf, pb, oacc[db]);
     }
+    fp8_mfma_hold(vf, pb);
   };
   using Par0 = std::integral_constant<int, 0>;
   using Par1 = std::integral_constant<int, 1>;
