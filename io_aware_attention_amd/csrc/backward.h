@@ -515,9 +515,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
       }
     }
     // P / dS buffers: row = key in the block (128 bytes: 64 queries, two rows per
-    // 256-byte bank line), 16-byte chunk c of row r stored at chunk c ^ ((r / 2) % 8), so
-    // the 16 rows a 128-bit access serves at once hit distinct banks
-    auto pchunk = [](int r, int c) { return r * PROWB + 16 * (c ^ ((r >> 1) & 7)); };
+    // 256-byte bank line, bit 0 of the row picking the half), 16-byte chunk c of row r
+    // stored at chunk c ^ key(r), key(r) = ((r / 2) % 8) ^ 4 (r % 2).  Phase 1 writes and
+    // phase 2 reads both have lane (n, H) on row n, chunk c0 + H.  The hardware serves a
+    // 128-bit write eight consecutive lanes at a time and a 128-bit read in four groups
+    // of 16 lanes (lane bit 5 and the parity of lane bits 2-4 fixed), each group needing
+    // distinct bank slots; measured on these exact access patterns, this key gives no bank
+    // conflicts for either, where (r / 2) % 8 cost 8 conflict cycles per write.
+    auto pchunk = [](int r, int c) {
+      const int key = ((r >> 1) & 7) ^ ((r & 1) << 2);
+      return r * PROWB + 16 * (c ^ key);
+    };
     const int prow = 32 * kb + n;
     int pwr[2], prd[4];  // phase 1 writes (queries 32qb + 16half + 8H ..), phase 2 reads
 #pragma unroll
