@@ -324,6 +324,15 @@ int launch_prefill(ff::FwdParams& p, int d, int causal, float scale, void* strea
   if (total >= kMaxElems) return FF_ERR_SHAPE;
   p.total = (int)total;
   p.scale_log2 = scale * ff::kLog2e;
+  // Causal grids that are resident all at once (two workgroups per CU at d = 128, three at
+  // d = 64) take their items in snake order over the CUs of each XCD.
+  p.snake = 0;
+  if (causal) {
+    int cus = 0;
+    const int st = device_cu_count(&cus);
+    if (st) return st;
+    if (cus % 8 == 0 && total <= (int64_t)cus * (d == 64 ? 3 : 2)) p.snake = cus / 8;
+  }
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
   if (d == 128) {

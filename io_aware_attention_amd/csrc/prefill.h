@@ -42,6 +42,7 @@
 #include <utility>
 
 #include "device.h"
+#include "tiles.h"
 
 namespace ff {
 
@@ -55,6 +56,7 @@ struct FwdParams {
   int num_m;                  // query tiles per (batch, head)
   int total;                  // 8 * u_per * G * num_m workgroups
   int u_per;                  // (batch, kv head) unit slots per XCD: ceil(B * Hkv / 8)
+  int snake;                  // CUs per XCD when the whole grid is resident at once, else 0
   float scale_log2;           // scale * log2(e)
   // Variable-length batches: when cu_q is set, q/o are [total_q, Hq, d], k/v are
   // [total_k, Hkv, d], sequence b owns rows cu_q[b] .. cu_q[b+1]-1 (keys: cu_k), Sq is
@@ -92,6 +94,25 @@ __device__ __forceinline__ int xcd_remap(int w, int total) {
   const int x = w % kXcd, k = w / kXcd;
   const int q = total / kXcd, r = total % kXcd;
   return x * q + (x < r ? x : r) + k;
+}
+
+// Work item of workgroup w.  A grid that is resident all at once gets no second round in
+// which short items could fill in behind long ones, and the dispatcher gives the c-th
+// workgroup of an XCD to CU c mod C, again and again.  With the work list heaviest
+// first, CU 0 would then collect the longest item of every round.  For such grids
+// (snake = C) every other round runs backwards, so a CU's long item of one round is
+// followed by a short one of the next.
+__device__ __forceinline__ int work_index(int w, int total, int snake) {
+  if (!snake) return xcd_remap(w, total);
+  constexpr int kXcd = 8;
+  const int x = w % kXcd, k = w / kXcd;
+  const int q = total / kXcd, r = total % kXcd;
+  const int len = q + (x < r);
+  const int round = k / snake, j = k - round * snake;
+  const int left = len - round * snake;
+  const int m = left < snake ? left : snake;  // items in this round
+  const int kk = (round & 1) ? round * snake + (m - 1 - j) : k;
+  return x * q + (x < r ? x : r) + kk;
 }
 
 template <bool B>
@@ -157,7 +178,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
   // one sequence spread over the XCDs and sequences of different length load them
   // evenly.  Inside an XCD the order is query tile (heaviest first when causal), then
   // unit, then query head of the unit, so each XCD starts its longest tiles first.
-  const int idx = xcd_remap(blockIdx.x, p.total);
+  const int idx = work_index(blockIdx.x, p.total, p.snake);
   const int grp = p.u_per * p.G * p.num_m;
   const int sg = idx / grp;
   const int r0 = idx - sg * grp;
@@ -195,45 +216,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
   const int qrow = q0 + wave * 32 + n;
 
   // ---- key-tile range (causal clipping: never visit tiles above the diagonal)
-  const int nb_total = (Sk + BN - 1) / BN;
-  int n_max = nb_total;
-  const int last_q = (q0 + BM < Sq ? q0 + BM : Sq) - 1;
-  if (CAUSAL) {
-    const int lim = last_q + Sk - Sq;
-    n_max = lim < 0 ? 0 : ((lim / BN + 1) < n_max ? lim / BN + 1 : n_max);
-  }
-  // Tiles [n_mask_lo, n_max) need an element mask (key tail or causal diagonal).
-  int n_mask_lo = (Sk % BN) ? nb_total - 1 : nb_total;
-  if (CAUSAL) {
-    const int first = q0 + Sk - Sq + 1;
-    const int tm = first <= 0 ? 0 : first / BN;
-    n_mask_lo = tm < n_mask_lo ? tm : n_mask_lo;
-  }
-  // Window: tiles [n_min, n_max) hold keys some row of the tile sees; tiles below n_bot
-  // hold keys left of the last row's window and need the element mask too.
-  int n_min = 0, n_bot = 0;
-  if constexpr (WIN) {
-    // 64-bit positions (a window may reach past 2^31); tile numbers by shifts, which stay
-    // scalar, of non-negative values
-    constexpr int LB = __builtin_ctz(BN);
-    static_assert((1 << LB) == BN, "BN must be a power of two");
-    if (p.wr >= 0) {
-      const int64_t lim = (int64_t)last_q + Sk - Sq + p.wr;  // right limit of the last row
-      const int64_t nm = lim < 0 ? 0 : (lim >> LB) + 1;
-      n_max = nm < n_max ? (int)nm : n_max;
-      const int64_t first = (int64_t)q0 + Sk - Sq + p.wr + 1;  // first key row q0 misses
-      const int64_t tm = first <= 0 ? 0 : first >> LB;
-      n_mask_lo = tm < n_mask_lo ? (int)tm : n_mask_lo;
-    }
-    if (p.wl >= 0) {
-      const int64_t lo_first = (int64_t)q0 + Sk - Sq - p.wl;    // left limit of row q0
-      const int64_t lo_last = (int64_t)last_q + Sk - Sq - p.wl; // left limit of the last row
-      n_min = lo_first <= 0 ? 0 : (int)(lo_first >> LB);
-      const int64_t nb = lo_last <= 0 ? 0 : (lo_last + BN - 1) >> LB;
-      n_bot = (int)(nb < n_max ? nb : n_max);
-      n_bot = n_bot > n_min ? n_bot : n_min;
-    }
-  }
+  const KeyTiles kt = key_tiles<BM, BN, CAUSAL, WIN>(q0, Sq, Sk, p.wl, p.wr);
+  const int n_max = kt.n_max, n_mask_lo = kt.n_mask_lo, n_min = kt.n_min, n_bot = kt.n_bot;
 
   const int64_t q_stride = (int64_t)p.Hq * D;    // elements between query positions
   const int kv_row_bytes = p.Hkv * D * 2;        // bytes between key positions
