@@ -9,7 +9,9 @@
  * enqueued on `stream` (a hipStream_t; NULL means the null stream) and runs
  * asynchronously; device faults surface at the caller's next synchronisation
  * with that stream.  Calls are re-entrant.  There is no fallback path: an
- * unsupported shape is an error, never a slower route.
+ * unsupported shape is an error, never a slower route.  Diagnostics: with the
+ * environment variable FLASHFWD_LOG set (to anything but "0"), every launch prints
+ * one line on stderr naming its kernel, grid and tile or split plan.
  *
  * Layouts (the pages' [batch, seqlen, heads, head_dim] convention: "flash
  * attention V2 code walk-through", tensor-shape table), all row-major and
@@ -122,7 +124,9 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, float* o, float
  * Here units = B * Hkv * ceil(Sq * (Hq/Hkv) / 16) workgroups per split and
  * slots = num_cus (one split workgroup per CU), and S is capped so every
  * split keeps at least 4 key blocks of FF_SPLIT_BLOCK_N.  num_cus <= 0 queries
- * the current device.  Pure host arithmetic apart from that query.
+ * the current device.  Pure host arithmetic apart from that query.  For benchmark
+ * sweeps only, the environment variable FLASHFWD_NUM_SPLITS = n (an integer in
+ * [1, FF_MAX_SPLITS]) replaces the rule's choice; other values are ignored.
  * Returns S >= 1, or the negated ff_status on invalid arguments. */
 int attn_splitkv_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int d, int num_cus);
 

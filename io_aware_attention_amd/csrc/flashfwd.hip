@@ -6,7 +6,10 @@
 // prefill.h and splitkv.h.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include <atomic>
 
@@ -30,6 +33,26 @@ constexpr int kSplitWgPerCu = 1;
 constexpr int kMinBlocksPerSplit = 4;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Opt-in trace of the host's plans: with FLASHFWD_LOG set to anything but "0", every
+// launch prints its kernel, grid and tiling or split decisions on stderr.
+bool log_on() {
+  static const bool on = [] {
+    const char* e = getenv("FLASHFWD_LOG");
+    return e && *e && !(e[0] == '0' && e[1] == 0);
+  }();
+  return on;
+}
+
+__attribute__((format(printf, 1, 2))) void plan_log(const char* fmt, ...) {
+  if (!log_on()) return;
+  va_list ap;
+  va_start(ap, fmt);
+  fputs("[flashfwd] ", stderr);
+  vfprintf(stderr, fmt, ap);
+  fputc('\n', stderr);
+  va_end(ap);
+}
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -169,6 +192,8 @@ template <int D>
 void launch_bwd(bool causal, int var, dim3 g_dq, dim3 g_dkdv, hipStream_t s,
                 const ff::BwdParams& p) {
   using namespace ff;
+  plan_log("attn_bwd d=%d causal=%d var=%d: attn_bwd_dq %u workgroups of 256 threads, then "
+           "attn_bwd_dkdv %u workgroups of 512 threads", D, (int)causal, var, g_dq.x, g_dkdv.x);
   constexpr int W = kVarWindow, WA = kVarWindow | kVarAlibi;
   if (causal) {
     if (var == 0) launch_bwd_var<D, true, 0>(g_dq, g_dkdv, s, p);
@@ -333,6 +358,10 @@ int launch_prefill(ff::FwdParams& p, int d, int causal, float scale, void* strea
     if (st) return st;
     if (cus % 8 == 0 && total <= (int64_t)cus * (d == 64 ? 3 : 2)) p.snake = cus / 8;
   }
+  plan_log("attn_fwd_prefill d=%d causal=%d var=%d%s: %lld workgroups of 256 threads, "
+           "query tiles of 128 rows x key tiles of 64, %d query tiles x %d unit slots per XCD "
+           "x %d query heads per kv head, snake=%d", d, causal, var, p.cu_q ? " varlen" : "",
+           (long long)total, p.num_m, p.u_per, p.G, p.snake);
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
   if (d == 128) {
@@ -458,6 +487,15 @@ int attn_splits_efficiency_rule(int units, int slots, int max_splits) {
 int attn_splitkv_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int d, int num_cus) {
   int st = check_dims(B, Sq, Sk, Hq, Hkv, d);
   if (st) return -st;
+  // benchmark sweeps: FLASHFWD_NUM_SPLITS=n (1 .. FF_MAX_SPLITS) replaces the rule
+  if (const char* e = getenv("FLASHFWD_NUM_SPLITS")) {
+    char* end = nullptr;
+    const long n = strtol(e, &end, 10);
+    if (end != e && *end == 0 && n >= 1 && n <= FF_MAX_SPLITS) {
+      plan_log("attn_splitkv_num_splits: %ld from FLASHFWD_NUM_SPLITS", n);
+      return (int)n;
+    }
+  }
   if (num_cus <= 0 && (st = device_cu_count(&num_cus))) return -st;
   const int64_t rows = (int64_t)Sq * (Hq / Hkv);
   const int64_t units = (int64_t)B * Hkv * cdiv(rows, kSplitRows);
@@ -466,8 +504,12 @@ int attn_splitkv_num_splits(int B, int Sq, int Sk, int Hq, int Hkv, int d, int n
   if (max_splits > FF_MAX_SPLITS) max_splits = FF_MAX_SPLITS;
   if (max_splits < 1) max_splits = 1;
   const int64_t slots = (int64_t)num_cus * kSplitWgPerCu;
-  if (units >= slots) return 1;
-  return attn_splits_efficiency_rule((int)units, (int)slots, (int)max_splits);
+  const int n = units >= slots
+                    ? 1
+                    : attn_splits_efficiency_rule((int)units, (int)slots, (int)max_splits);
+  plan_log("attn_splitkv_num_splits: %d (%lld workgroups per split, %lld slots, at most %lld "
+           "splits)", n, (long long)units, (long long)slots, (long long)max_splits);
+  return n;
 }
 
 int attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o_accum,
@@ -518,6 +560,9 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, float* o_accum
   p.scale_log2 = scale * ff::kLog2e;
   const int64_t total = (int64_t)B * Hkv * p.num_mb * num_splits;
   if (total >= kMaxElems) return FF_ERR_SHAPE;
+  plan_log("attn_fwd_splitkv d=%d causal=%d: %lld workgroups = %d batches x %d kv heads x %d "
+           "row blocks of %d folded rows x %d splits of %d keys", d, p.causal, (long long)total,
+           B, Hkv, p.num_mb, kSplitRows, num_splits, p.split_keys);
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
   if (d == 128) hipLaunchKernelGGL((ff::attn_fwd_splitkv<128, false, 0>), grid, block, 0, s, p);
@@ -627,6 +672,10 @@ int fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
   set_variant(p, var, scale);
   const int64_t total = (int64_t)B * Hkv * p.num_mb * num_splits;
   if (total >= kMaxElems) return FF_ERR_SHAPE;
+  plan_log("attn_fwd_splitkv (key/value cache%s) d=%d causal=%d var=%d: %lld workgroups = %d "
+           "batches x %d kv heads x %d row blocks of %d folded rows x %d splits",
+           block_table ? ", paged" : "", d, p.causal, var.var, (long long)total, B, Hkv,
+           p.num_mb, kSplitRows, num_splits);
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
   if (d == 128) launch_cache_var<128>(var.var, grid, block, s, p);
@@ -705,6 +754,8 @@ int attn_kvcache_append(const void* k_new, const void* v_new, void* k_cache, voi
   p.page = page_size;
   p.max_blocks = block_table ? max_blocks_per_seq : 1;
   p.chunks = new_elems / 8;
+  plan_log("attn_kvcache_append d=%d: %lld 16-byte chunks, %lld workgroups", d,
+           (long long)p.chunks, (long long)cdiv(p.chunks, 256));
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)cdiv(p.chunks, 256)), block(256);
   if (d == 128) hipLaunchKernelGGL(ff::attn_kvcache_append<128>, grid, block, 0, s, p);
@@ -737,6 +788,8 @@ int attn_splitkv_combine(const float* o_accum, const float* lse_accum, float* o,
   p.Hq = Hq;
   p.num_splits = num_splits;
   p.rows = (int)rows;
+  plan_log("attn_splitkv_combine d=%d: %lld rows x %d splits, %lld workgroups", d,
+           (long long)rows, num_splits, (long long)cdiv(rows, 4));
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)cdiv(rows, 4)), block(256);
   if (d == 128) hipLaunchKernelGGL(ff::attn_splitkv_combine<128>, grid, block, 0, s, p);
@@ -827,6 +880,8 @@ int attn_quantize_fp8(const void* x, void* x_fp8, float* scales, int B, int S, i
   p.H = H;
   p.nblk = nblk;
   p.rotate = rotate ? 1 : 0;
+  plan_log("attn_quantize_fp8 d=%d: %lld workgroups = %d batches x %d heads x %d blocks of "
+           "positions", d, (long long)B * H * nblk, B, H, nblk);
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)((int64_t)B * H * nblk)), block(256);
   if (d == 128) hipLaunchKernelGGL(ff::attn_quantize_fp8<128>, grid, block, 0, s, p);
@@ -879,6 +934,9 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_sca
   p.nqb = nqb;
   p.nkb = nkb;
   p.scale_log2 = scale * ff::kLog2e;
+  plan_log("attn_fwd_fp8 d=%d causal=%d: %lld workgroups of 256 threads, %d query tiles x %d "
+           "unit slots per XCD x %d query heads per kv head", d, causal, (long long)total,
+           p.num_m, p.u_per, p.G);
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)total), block(256);
   if (d == 128) {

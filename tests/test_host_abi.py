@@ -329,3 +329,27 @@ def call_noalloc(q=Q, k=K, v=V, o=O, lse=L, **kw):
 ])
 def test_attn_fwd_splitkv_noalloc_rejects(kw, code):
     assert call_noalloc(**kw) == code
+
+
+def _run_with_env(code, env):
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       env=dict(os.environ, **env), timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return r.stdout, r.stderr
+
+
+def test_plan_log_and_split_override():
+    """FLASHFWD_LOG prints the host's plan; FLASHFWD_NUM_SPLITS (benchmark sweeps) replaces
+    the split rule's choice when it is an integer in [1, FF_MAX_SPLITS], else is ignored."""
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from io_aware_attention_amd import flashfwd as f\n"
+            "print(f.attn_splitkv_num_splits(8, 1, 32768, 32, 8, 128, 256))\n" % ROOT)
+    base, err = _run_with_env(code, {"FLASHFWD_LOG": "0", "FLASHFWD_NUM_SPLITS": ""})
+    assert err == ""
+    out, err = _run_with_env(code, {"FLASHFWD_LOG": "1", "FLASHFWD_NUM_SPLITS": ""})
+    assert out == base and f"attn_splitkv_num_splits: {int(base)}" in err
+    out, err = _run_with_env(code, {"FLASHFWD_LOG": "1", "FLASHFWD_NUM_SPLITS": "7"})
+    assert int(out) == 7 and "from FLASHFWD_NUM_SPLITS" in err
+    for bad in ("0", "-3", "x", "9999", "5x"):
+        out, _ = _run_with_env(code, {"FLASHFWD_NUM_SPLITS": bad})
+        assert out == base, bad
