@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace ff {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -136,6 +138,16 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 __device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
+
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, fully unrolled.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
 
 // Mask and bias variants of the forward kernels (their VAR template argument), after the
 // walk-through's Is_local, Has_alibi and Is_softcap flags: the sliding window (window

@@ -120,16 +120,6 @@ struct MaskTag {
   static constexpr bool value = B;
 };
 
-template <int N, typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-// f(integral_constant<int, i>) for i = 0 .. N-1, fully unrolled.
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
-}
-
 // The two transposing reads of GEMM1 fragment i = (kb, db, cp): keys
 // 32kb + 16cp + {0..3, 4..7} of the V tile, dcols 32db + lane's column.
 template <int I, int D, int ROWB>

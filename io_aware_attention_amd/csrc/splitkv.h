@@ -15,8 +15,8 @@
 //   O^T (16 dcols x 16 rows) += V^T . P^T, 32 keys per instruction
 // The key rows of the two 16-key blocks are interleaved so that each lane's
 // eight scores are eight consecutive keys, which makes them the P^T operand
-// as they stand.  V goes through a per-wavefront LDS area, transposed on the
-// way in, so V^T fragments are single 128-bit LDS reads.
+// as they stand.  V goes through a per-wavefront LDS area row by row, as loaded,
+// and GEMM1's V^T fragments come out of it through transposing reads.
 //
 // Variants (VAR != 0, cache kernels only; the walk-through's Is_local, Has_alibi,
 // Is_softcap): with diag = i + Sk - Sq for query i, the window keeps keys
@@ -75,20 +75,26 @@ struct SplitTraits {
   static constexpr int BMD = 16;                  // folded rows per workgroup
   static constexpr int TK = 32;                   // keys per wavefront step
   static constexpr int kWaves = 4;
-  // V^T layout in a wavefront's LDS area: dcol j, 16-byte chunk ch (keys 8 ch .. +7) at
-  //   GS (j >> 3) + 64 (j & 7) + 16 (ch ^ (((j >> 2) ^ ((j >> 5) << SH)) & 3)),
-  // SH = 1 at d = 64, else 0.  Each group of 8 dcol rows (64 bytes each) is padded to
-  // GS = 576 bytes, so the groups start at four different bank offsets, and the chunk
-  // XOR spreads the rows that share an offset over the row.  The transposing writes (per
-  // lane 8 dcols of 4 keys: eight 8-byte writes to dcol rows 8 apart) then reach every
-  // LDS bank twice, the minimum, where plain 80-byte rows put 16 lanes on two bank
-  // offsets (an 8-way conflict); the 16-byte reads of GEMM1 stay conflict-free.  Row
-  // offsets within a group are additive, so they fold into the instructions' offsets.
-  static constexpr int GS = 576;
-  static constexpr int SH = D == 64 ? 1 : 0;
-  static constexpr int WV = (D / 8) * GS;          // V^T area per wavefront
+  // V rows in a wavefront's LDS area: key row r of the step at RS p(r) bytes, p(r) = r
+  // with its bits 2 and 3 exchanged, RS = the row's bytes + 32.  The 32-byte pad moves
+  // consecutive slots 32 bytes along the 256-byte bank line (RS / 32 is odd), and the
+  // exchange puts the eight rows that one half-wavefront's transposing read touches
+  // (rows j and 8 + j, j < 4, of its two 16-lane groups; + 4 for the second read) on
+  // eight consecutive slots: 32 lanes x 8 bytes then cover the line once.  A 128-bit row
+  // write by 8 consecutive lanes is 128 contiguous bytes.  Row r + i (i < 4) of a 4-row
+  // group is slot p(r) + i, and the second read's rows are slot + 8, so every address
+  // is one per-lane base plus an immediate.
+  static constexpr int RS = 2 * D + 32;
+  static constexpr int WV = TK * RS;               // V area per wavefront
+  static __device__ __forceinline__ int slot(int r) {
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+  }
   static constexpr int VB = TK * D / 8 / 4 / 64;  // 4-key x 8-dcol V blocks per lane
-  static constexpr int kCombine = kWaves * (2 * BMD + BMD * D) * 4;
+  // The merge's partial O rows, padded by 4 floats: at D floats a row is a multiple of
+  // the 256-byte bank line, and the 16 rows one write instruction spreads over would
+  // all start on the same bank.
+  static constexpr int CD = D + 4;
+  static constexpr int kCombine = kWaves * (2 * BMD + BMD * CD) * 4;
   static constexpr int kLds = kWaves * WV > kCombine ? kWaves * WV : kCombine;
 };
 
@@ -208,24 +214,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   const int64_t brow = CACHE ? 0 : (int64_t)b * Sk;
   const uint16_t* kbase = p.k + brow * kv_stride + (int64_t)hk * D;
   const uint16_t* vbase = p.v + brow * kv_stride + (int64_t)hk * D;
-  char* wv = smem + wave * T::WV;
-  // V^T addresses (the layout in SplitTraits).  Writes: base of dcols 8 cg + 4 h .. + 3
-  // of this lane's key block; dcol 8 cg + c is at vt_w[bi][c >> 2] + 64 (c & 3).  Reads
-  // (GEMM1's A operand, dcol 16 db + nr, chunk g4): 2 GS db + vt_r[chunk key of db].
-  int vt_w[VB][2];
+  const uint32_t wv = lds_addr(smem) + wave * T::WV;
+  // V addresses (the layout in SplitTraits).  Writes: row 4 kg + r, 16-byte chunk cg of
+  // this lane's loads at vw[bi] + RS r.  Reads: GEMM1's A operand for dcols 16 db ..
+  // + 15 is two ds_read_b64_tr_b16.  In each 16-lane group g4, source lane nr addresses
+  // key row 8 g4 + nr / 4 (+ 4 for the second read) at dcols 16 db + 4 (nr % 4) .. + 3,
+  // so result lane nr holds dcol 16 db + nr over keys 8 g4 .. + 3 (+ 4 .. + 7): the A
+  // fragment V^T[16 db + nr][8 g4 .. + 7].
+  int vw[VB];
 #pragma unroll
   for (int bi = 0; bi < VB; ++bi) {
     const int blk = lane + 64 * bi;
     const int cg = blk % (D / 8), kg = blk / (D / 8);
-    const int k0 = ((2 * cg) ^ ((cg >> 2) << T::SH)) & 3;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      vt_w[bi][h] = T::GS * cg + 256 * h + 16 * ((kg >> 1) ^ k0 ^ h) + 8 * (kg & 1);
+    vw[bi] = T::slot(4 * kg) * T::RS + 16 * cg;
   }
-  int vt_r[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    vt_r[k] = T::GS * (nr >> 3) + 64 * (nr & 7) + 16 * (g4 ^ ((nr >> 2) & 3) ^ k);
+  const int vr = T::slot(8 * g4 + (nr >> 2)) * T::RS + 8 * (nr & 3);
 
   f32x4 oacc[D / 16];
 #pragma unroll
@@ -339,31 +342,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
     for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
     const u32x4 pf = pack8(sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1],
                            sc[1][2], sc[1][3]);
-    // V -> V^T in this wavefront's LDS area: dcol 8 cg + c of keys 4 kg .. 4 kg + 3
+    // V rows into this wavefront's LDS area, as loaded
 #pragma unroll
     for (int bi = 0; bi < VB; ++bi) {
+      typedef __attribute__((address_space(3))) char lds_char;
+      lds_char* row0 = (lds_char*)(uintptr_t)(wv + vw[bi]);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int dw = c >> 1;
-        u32x2 val;
-        if (c & 1) {
-          val[0] = hi_hi(vreg[bi][0][dw], vreg[bi][1][dw]);
-          val[1] = hi_hi(vreg[bi][2][dw], vreg[bi][3][dw]);
-        } else {
-          val[0] = lo_lo(vreg[bi][0][dw], vreg[bi][1][dw]);
-          val[1] = lo_lo(vreg[bi][2][dw], vreg[bi][3][dw]);
-        }
-        *reinterpret_cast<u32x2*>(wv + vt_w[bi][c >> 2] + 64 * (c & 3)) = val;
-      }
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(row0 + T::RS * r) =
+            vreg[bi][r];
     }
     wave_lds_sync();
     // O^T += V^T . P^T; A operand: V^T[16 db + nr][8 g4 .. +7]
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(
-          wv + 2 * T::GS * db + vt_r[((db >> 1) << T::SH) & 3]);
-      oacc[db] = mfma16(a, pf, oacc[db]);
-    }
+    static_for<D / 16>([&](auto DB) {
+      constexpr int db = decltype(DB)::value;
+      const u32x2 lo = ds_read_tr16_b64<32 * db>(wv + vr);
+      const u32x2 hi = ds_read_tr16_b64<32 * db + 8 * T::RS>(wv + vr);
+      oacc[db] = mfma16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, oacc[db]);
+    });
     wave_lds_sync();
   };
   // The prefetch is unconditional (a conditional one would make the compiler wait
@@ -400,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   }
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
-    st16f(co + (wave * 16 + nr) * D + 16 * db + 4 * g4, oacc[db]);
+    st16f(co + (wave * 16 + nr) * T::CD + 16 * db + 4 * g4, oacc[db]);
   __syncthreads();
 
   constexpr int DPT = D / 16;  // dcols per thread in the merge
@@ -422,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   for (int c = 0; c < DPT; ++c) {
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) acc += co[(w * 16 + row) * D + dc0 + c] * wgt[w];
+    for (int w = 0; w < NW; ++w) acc += co[(w * 16 + row) * T::CD + dc0 + c] * wgt[w];
     out[c] = acc * inv;
   }
   const float lse_val = L > 0.f ? (M + fast_log2(L)) * kLn2 : -INFINITY;
