@@ -3,12 +3,14 @@
  *
  * C ABI.  Every tensor argument is a device pointer owned by the caller; the
  * library never allocates, frees or synchronises, and keeps no mutable global
- * state apart from a per-device cache of the compute-unit count.  Each call
- * checks all of its arguments before enqueueing anything: on a non-zero return
- * nothing was enqueued and no output was touched.  On success the work is
- * enqueued on `stream` (a hipStream_t; NULL means the null stream) and runs
- * asynchronously; device faults surface at the caller's next synchronisation
- * with that stream.  Calls are re-entrant.  There is no fallback path: an
+ * state apart from a per-device cache of the compute-unit count and of the address
+ * of attn_fwd_splitkv_noalloc's static device buffer.  Each call checks all of its
+ * arguments before enqueueing anything: on a non-zero return nothing was enqueued
+ * and no output was touched.  On success the work is enqueued on `stream` (a
+ * hipStream_t; NULL means the null stream) and runs asynchronously; device faults
+ * surface at the caller's next synchronisation with that stream.  Calls are
+ * re-entrant, except that overlapping attn_fwd_splitkv_noalloc calls on one GPU share
+ * its buffer (see there).  There is no fallback path: an
  * unsupported shape is an error, never a slower route.  Diagnostics: with the
  * environment variable FLASHFWD_LOG set (to anything but "0"), every launch prints
  * one line on stderr naming its kernel, grid and tile or split plan.
