@@ -374,19 +374,37 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
   issue_k(t);
   issue_v(t);
   issue_k(t - 1);
+  // Masked steps: those whose next tile needs the element mask, rounded up to even.
+  const int n_next = n_max - 1 - n_min;  // steps that have a next tile
+  int n_masked = n_next - (n_mask_lo > n_min ? n_mask_lo - n_min : 0);
+  n_masked = n_masked < 0 ? 0 : (n_masked > n_next ? n_next : n_masked);
+  // On the causal diagonal the first tile visited can lie wholly right of every row of a
+  // wavefront (the lower half of the query tile, when the tile edges line up).  Such a
+  // wavefront skips that tile's products and exponentials; it still takes part in the
+  // step's loads and barriers, and its state stays (m, l, o) = (-inf, 0, 0).  Only the
+  // first pair of masked steps, which the loop below peels, can take this path.
+  bool skip_first = false;
+  if constexpr (CAUSAL) {
+    const int w_rows_end = q0 + 32 * __builtin_amdgcn_readfirstlane(wave) + 32;  // wave-uniform
+    const int w_last_row = (w_rows_end < Sq ? w_rows_end : Sq) - 1;
+    skip_first = n_masked > 0 && t - n_min >= 2 && w_last_row + Sk - Sq < t * BN;
+  }
   wait_vmem();  // Q in registers, this wave's share of the tiles in LDS
   __syncthreads();
   // Scores of two consecutive tiles: in a step of parity P, S[P] holds tile t's and
   // S[P ^ 1] receives tile t-1's; the roles swap every step, so nothing is copied.
   f32x16 S[2][2];
-  gemm0(kbuf(t), S[0]);
-  if constexpr (LOGIT) {
-    const float rb = rbase(t);
+  float mx = -INFINITY;
+  if (!skip_first) {
+    gemm0(kbuf(t), S[0]);
+    if constexpr (LOGIT) {
+      const float rb = rbase(t);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) S[0][e >> 4][e & 15] = logit(S[0][e >> 4][e & 15], e, rb);
+      for (int e = 0; e < 32; ++e) S[0][e >> 4][e & 15] = logit(S[0][e >> 4][e & 15], e, rb);
+    }
+    if (t >= n_mask_lo || t < n_bot) mask(S[0], t);
+    mx = rowmax(S[0]);
   }
-  if (t >= n_mask_lo || t < n_bot) mask(S[0], t);
-  float mx = rowmax(S[0]);
   // Every wave has read K of the first tile before the first step refills its buffer.
   __syncthreads();
 
@@ -398,10 +416,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
   // issues every LDS read just before its use).
   constexpr int NG0 = 2 * (D / 16);  // GEMM0 MFMAs: (c, kb), kb fastest
   constexpr int NG1 = 4 * (D / 32);  // GEMM1 MFMAs: (kb, db, cp)
-  auto step = [&](auto par_tag, int t, auto has_next_tag, auto mask_next_tag) {
+  auto step = [&](auto par_tag, int t, auto has_next_tag, auto mask_next_tag,
+                  auto skip_tag) {
     constexpr int P = decltype(par_tag)::value;
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
+    constexpr bool SKIP = decltype(skip_tag)::value;  // no visible key of tile t here
     f32x16(&sc)[2] = S[P];
     f32x16(&sn)[2] = S[P ^ 1];
     // reference point for tile t: raise it (and rescale o, l) only past the slack
@@ -450,14 +470,16 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
         sn[i & 1] = mfma32(kr[i % 3], qf[i >> 1], sn[i & 1]);
       }
       constexpr int EPG = 32 / NG0;  // score elements per group
+      if constexpr (!SKIP) {
 #pragma unroll
-      for (int q = 0; q < EPG; ++q) {
-        const int e = i * EPG + q;  // 0..31: block e / 16, element e % 16
-        const float x = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], cexp, -m_use));
-        sc[e >> 4][e & 15] = x;
-        lsum[q & 3] += x;
+        for (int q = 0; q < EPG; ++q) {
+          const int e = i * EPG + q;  // 0..31: block e / 16, element e % 16
+          const float x = fast_exp2(__builtin_fmaf(sc[e >> 4][e & 15], cexp, -m_use));
+          sc[e >> 4][e & 15] = x;
+          lsum[q & 3] += x;
+        }
       }
-      if constexpr (((i + 1) * EPG) % 8 == 0) {  // eight more probabilities: pack them
+      if constexpr (!SKIP && ((i + 1) * EPG) % 8 == 0) {  // eight more probabilities: pack them
         constexpr int e0 = (i + 1) * EPG - 8;
         const f32x16& b = sc[e0 >> 4];
         constexpr int o = e0 & 15;
@@ -465,24 +487,29 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
       }
       __builtin_amdgcn_sched_barrier(0);
     });
-    l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    if constexpr (!SKIP) l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 
     // -- block B: PV of tile t interleaved with mask and row max of tile t-1
     __builtin_amdgcn_s_setprio(0);
     const uint32_t vl = smem_addr + (2 + P) * TILE;  // V of tile t
     u32x2 flo[3], fhi[3];
-    gemm1_read<0, D, ROWB>(vl, va, flo[0], fhi[0]);
-    gemm1_read<1, D, ROWB>(vl, va, flo[1], fhi[1]);
+    if constexpr (!SKIP) {
+      gemm1_read<0, D, ROWB>(vl, va, flo[0], fhi[0]);
+      gemm1_read<1, D, ROWB>(vl, va, flo[1], fhi[1]);
+    }
     const int vln = vis_lim(t - 1);
     const int vlon = vis_lo(t - 1);
     const float rbn = LOGIT ? rbase(t - 1) : 0.f;
     float mxn = -INFINITY;
     static_for<NG1>([&](auto I) {
       constexpr int i = decltype(I)::value;
-      if constexpr (i + 2 < NG1) gemm1_read<i + 2, D, ROWB>(vl, va, flo[(i + 2) % 3], fhi[(i + 2) % 3]);
-      const u32x4 a = {flo[i % 3][0], flo[i % 3][1], fhi[i % 3][0], fhi[i % 3][1]};
-      constexpr int kb = i / (NG1 / 2), db = (i % (NG1 / 2)) / 2, cp = i % 2;
-      oacc[db] = mfma32(a, pf[kb][cp], oacc[db]);
+      if constexpr (!SKIP) {
+        if constexpr (i + 2 < NG1)
+          gemm1_read<i + 2, D, ROWB>(vl, va, flo[(i + 2) % 3], fhi[(i + 2) % 3]);
+        const u32x4 a = {flo[i % 3][0], flo[i % 3][1], fhi[i % 3][0], fhi[i % 3][1]};
+        constexpr int kb = i / (NG1 / 2), db = (i % (NG1 / 2)) / 2, cp = i % 2;
+        oacc[db] = mfma32(a, pf[kb][cp], oacc[db]);
+      }
       if constexpr (HAS_NEXT) {
         constexpr int EPG = 32 / NG1;
 #pragma unroll
@@ -513,28 +540,33 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
   using Par1 = std::integral_constant<int, 1>;
   using Yes = MaskTag<true>;
   using No = MaskTag<false>;
-  const int n_next = n_max - 1 - n_min;  // steps that have a next tile
-  int n_masked = n_next - (n_mask_lo > n_min ? n_mask_lo - n_min : 0);
-  n_masked = n_masked < 0 ? 0 : (n_masked > n_next ? n_next : n_masked);
-  for (int pair = 0; pair < (n_masked + 1) / 2 && t - n_min >= 2; ++pair, t -= 2) {
-    step(Par0{}, t, Yes{}, Yes{});
-    step(Par1{}, t - 1, Yes{}, Yes{});
+  int pair = 0;
+  if (n_masked > 0 && t - n_min >= 2) {  // the first masked pair, peeled
+    if (skip_first) step(Par0{}, t, Yes{}, Yes{}, Yes{});
+    else step(Par0{}, t, Yes{}, Yes{}, No{});
+    step(Par1{}, t - 1, Yes{}, Yes{}, No{});
+    pair = 1;
+    t -= 2;
+  }
+  for (; pair < (n_masked + 1) / 2 && t - n_min >= 2; ++pair, t -= 2) {
+    step(Par0{}, t, Yes{}, Yes{}, No{});
+    step(Par1{}, t - 1, Yes{}, Yes{}, No{});
   }
   for (; t - 2 >= n_bot; t -= 2) {  // both next tiles lie at or above n_bot
-    step(Par0{}, t, Yes{}, No{});
-    step(Par1{}, t - 1, Yes{}, No{});
+    step(Par0{}, t, Yes{}, No{}, No{});
+    step(Par1{}, t - 1, Yes{}, No{}, No{});
   }
   if constexpr (WIN) {
     for (; t - n_min >= 2; t -= 2) {
-      step(Par0{}, t, Yes{}, Yes{});
-      step(Par1{}, t - 1, Yes{}, Yes{});
+      step(Par0{}, t, Yes{}, Yes{}, No{});
+      step(Par1{}, t - 1, Yes{}, Yes{}, No{});
     }
   }
   if (t - n_min == 1) {
-    step(Par0{}, n_min + 1, Yes{}, Yes{});
-    step(Par1{}, n_min, No{}, No{});
+    step(Par0{}, n_min + 1, Yes{}, Yes{}, No{});
+    step(Par1{}, n_min, No{}, No{}, No{});
   } else {
-    step(Par0{}, n_min, No{}, No{});
+    step(Par0{}, n_min, No{}, No{}, No{});
   }
 
   // ---- epilogue: O = o / l, LSE = (m + log2 l) ln 2
