@@ -72,6 +72,21 @@ def test_prefill_key_tail_residues(ff, oracle, Sk, causal):
     check_outputs(o, lse, o_ref, lse_ref, f"Sk={Sk}")
 
 
+@pytest.mark.parametrize("offset", [0, 1, 31, 32, 33, 63, 64, 65, 96, 100])
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_causal_diagonal_offsets(ff, oracle, offset, d):
+    """Causal with Sk = Sq + offset: the diagonal crosses the 64-key tiles at every
+    alignment relative to the 128-row query tiles and their 32-row wavefronts, so the
+    first diagonal tile is invisible to one, two or none of a workgroup's wavefronts."""
+    B, Sq, Hq, Hkv = 1, 384, 2, 1
+    Sk = Sq + offset
+    say(f"prefill causal diagonal offset={offset} d={d}")
+    q, k, v = make_inputs(B, Sq, Sk, Hq, Hkv, d, seed=900 + offset + d)
+    o, lse = run_fwd(ff, q, k, v, True, 0.125)
+    o_ref, lse_ref = oracle.fwd(q, k, v, True, 0.125)
+    check_outputs(o, lse, o_ref, lse_ref, f"offset={offset} d={d}")
+
+
 def test_tiny_mha_workload_full(ff, oracle):
     w = synth.WORKLOADS["tiny_mha"]
     q, k, v = synth.make_qkv(w)
