@@ -139,6 +139,15 @@ __device__ __forceinline__ void wait_vmem() {
 
 __device__ __forceinline__ float sum_xor32(float x) { return x + __shfl_xor(x, 32); }
 
+// Wavefront-local LDS handoff: the lanes of one wavefront exchange data through
+// LDS; the fences order the accesses and the wave barrier keeps the compiler
+// from moving them across each other.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int N, typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);

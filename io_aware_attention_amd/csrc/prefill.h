@@ -569,23 +569,42 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
     step(Par0{}, n_min, No{}, No{}, No{});
   }
 
-  // ---- epilogue: O = o / l, LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = o / l, LSE = (m + log2 l) ln 2.  The rows leave through LDS: each
+  // wavefront stages its 32 normalised O rows in its own quarter of the tile buffers (all
+  // free once every wave is past its last step), the 16-byte chunks XOR-swizzled by row,
+  // and then stores whole rows, two (d = 128) or four (d = 64) per instruction, where
+  // storing from the product's layout writes 32 rows in 32-byte pieces per instruction.
+  // Both LDS passes are free of bank conflicts.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow < Sq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* orow = p.o + ((int64_t)q_start + qrow) * q_stride + (int64_t)h * D;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  constexpr int CH = D / 4;     // 16-byte chunks per O row
+  constexpr int OROWB = D * 4;  // bytes per O row
+  constexpr int RPI = 64 / CH;  // rows per store instruction
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  __syncthreads();
+  const uint32_t ost = smem_addr + wave * 32 * OROWB;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 val = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
-                           oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv};
-        st16f(orow + 32 * db + 8 * j + 4 * H, val);
-      }
-    if (H == 0)
-      p.lse[lse_base + qrow] =
-          l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 val = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
+                         oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv};
+      const int c = 8 * db + 2 * j + H;  // dcols 32 db + 8 j + 4 H .. + 3
+      *reinterpret_cast<lds_f32x4*>((uintptr_t)(ost + n * OROWB + 16 * (c ^ (n & 7)))) = val;
+    }
+  wave_lds_sync();
+  const int rr = lane / CH, cc = lane % CH;
+  const int row0 = q0 + 32 * wave;
+  float* obase = p.o + ((int64_t)q_start + row0) * q_stride + (int64_t)h * D + 4 * cc;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + rr;
+    const f32x4 val =
+        *reinterpret_cast<const lds_f32x4*>((uintptr_t)(ost + r * OROWB + 16 * (cc ^ (r & 7))));
+    if (row0 + r < Sq) st16f(obase + (int64_t)r * q_stride, val);
   }
+  if (qrow < Sq && H == 0)
+    p.lse[lse_base + qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
 #endif
 }
 

@@ -61,15 +61,6 @@ struct SplitParams {
   float cap_k, cap2;
 };
 
-// Wavefront-local LDS handoff: the lanes of one wavefront exchange data through
-// LDS; the fences order the accesses and the wave barrier keeps the compiler
-// from moving them across each other.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int D>
 struct SplitTraits {
   static constexpr int BMD = 16;                  // folded rows per workgroup
