@@ -323,9 +323,26 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fp8(Fp8Params p) {
   struct TileScale {
     float c2, lr, ir;
   };
+  // The block scales are held in registers, 64 blocks per window, lane l holding block
+  // bhi - 64 w - l of window w, and read with readlane: a scale loaded at the top of its
+  // step would make that step wait for the load's full latency (it joins the wait for
+  // the tile's own loads), which cost up to half of each step.  A window is reloaded
+  // once every 128 steps.
   const float inv_sv_max = 1.f / sv_max;
+  const int bhi = (n_max - 1) >> 1;
+  float ksw, vsw;
+  auto load_window = [&](int w) {
+    const int blk = bhi - 64 * w - lane;
+    ksw = blk >= 0 ? ks[blk] : 0.f;
+    vsw = blk >= 0 ? vs[blk] : 0.f;
+  };
+  load_window(0);
   auto tile_scale = [&](int t) {
-    const float sk = ks[t >> 1], r = vs[t >> 1] * inv_sv_max;
+    const int j = bhi - (t >> 1);  // wave-uniform
+    if ((j & 63) == 0 && j > 0) load_window(j >> 6);
+    const float sk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ksw), j & 63));
+    const float sv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vsw), j & 63));
+    const float r = sv * inv_sv_max;
     return TileScale{c2q * sk, fast_log2(r), __builtin_amdgcn_rcpf(r)};
   };
 

@@ -139,6 +139,9 @@ CASES = [
     (1, 1, 1000, 4, 2, 128, False, False),
     (2, 129, 129, 2, 2, 128, False, True),
     (1, 700, 700, 2, 1, 64, True, False),
+    # more than 64 key scale blocks: the kernel holds the block scales 64 at a time
+    (1, 130, 8500, 2, 1, 128, True, False),
+    (1, 64, 16500, 2, 2, 64, False, False),
 ]
 
 
