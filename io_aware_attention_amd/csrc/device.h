@@ -57,6 +57,14 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ void st16f(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+// The same with the non-temporal hint, for outputs that are written once and not read
+// back by the kernel: they stream through L2 without displacing the key/value tiles
+// that other workgroups are about to read.  Only for whole 128-byte lines: scattered
+// 16-byte pieces stored this way lose the write combining (an FP8 forward whose lanes
+// each stored 16 bytes of a row took 237 instead of 179 us).
+__device__ __forceinline__ void st16f_nt(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
