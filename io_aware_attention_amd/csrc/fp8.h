@@ -434,23 +434,51 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fp8(Fp8Params p) {
   }
   if (t == 0) step(Par0{}, 0, Yes{});
 
-  // ---- epilogue: O = sv_max o / l, LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = sv_max o / l, LSE = (m + log2 l) ln 2.  The rows leave through LDS
+  // as in the bf16 kernel, whole rows per store instruction with the non-temporal hint,
+  // but in two passes of PD dcols: the tile buffers hold 32 rows of PD fp32 values per
+  // wavefront.  Each staged row is a whole number of 128-byte lines, its 16-byte chunks
+  // XOR-swizzled by row (both LDS passes free of bank conflicts).
   fp8_mfma_drain(oacc);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow < Sq) {
-    const float inv = l_tot > 0.f ? sv_max / l_tot : 0.f;
-    float* orow = p.o + ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D;
+  const float inv = l_tot > 0.f ? sv_max / l_tot : 0.f;
+  constexpr int PD = T::kLds / (4 * 32 * 4);  // dcols per pass: 64 (d = 128), 32 (d = 64)
+  constexpr int PCH = PD / 4;                 // 16-byte chunks per staged row
+  constexpr int PROWB = PD * 4;               // bytes per staged row
+  constexpr int RPI = 64 / PCH;               // rows per store instruction
+  constexpr int DBP = PD / 32;                // accumulator blocks per pass
+  static_assert(D % PD == 0 && PD % 32 == 0 && PCH <= 16, "staging passes");
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  wait_vmem();      // the last step's (empty) tile loads have retired: LDS is not written again
+  __syncthreads();  // every wavefront is past its last read of the tiles
+  const uint32_t ost = smem_addr + wave * 32 * PROWB;
+  const int rr = lane / PCH, cc = lane % PCH;
+  const int row0 = q0 + 32 * wave;
+  float* obase = p.o + ((int64_t)b * Sq + row0) * q_stride + (int64_t)h * D + 4 * cc;
+  static_for<D / PD>([&](auto PS) {
+    constexpr int ps = decltype(PS)::value;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int dbp = 0; dbp < DBP; ++dbp)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const int db = ps * DBP + dbp;
         const f32x4 val = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
                            oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv};
-        st16f(orow + 32 * db + 8 * j + 4 * H, val);
+        const int c = 8 * dbp + 2 * j + H;  // dcols 32 db + 8 j + 4 H .. + 3 of this pass
+        *reinterpret_cast<lds_f32x4*>((uintptr_t)(ost + n * PROWB + 16 * (c ^ (n & 7)))) = val;
       }
-    if (H == 0)
-      p.lse[lse_base + qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
-  }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + rr;
+      const f32x4 val =
+          *reinterpret_cast<const lds_f32x4*>((uintptr_t)(ost + r * PROWB + 16 * (cc ^ (r & 7))));
+      if (row0 + r < Sq) st16f_nt(obase + (int64_t)r * q_stride + ps * PD, val);
+    }
+    wave_lds_sync();  // the next pass rewrites the staged rows
+  });
+  if (qrow < Sq && H == 0)
+    p.lse[lse_base + qrow] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
 #endif
 }
 
