@@ -357,17 +357,37 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
   }
   if (t < n_max) step(std::integral_constant<uint32_t, 0>{}, t);
 
-  // dQ = scale * dQ^T: element 4j + i of block db is dcol 32db + 8j + 4H + i
-  if (qrow < Sq) {
+  // dQ = scale * dQ^T: element 4j + i of block db is dcol 32db + 8j + 4H + i.  The rows
+  // leave through LDS as in the forward kernel (each wavefront stages its 32 rows in the
+  // tile buffers, 16-byte chunks XOR-swizzled by row) and are stored whole, with the
+  // non-temporal hint.
+  {
     const float sc = p.scale;
+    constexpr int CH = D / 4, OROWB = D * 4, RPI = 64 / CH;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    wait_vmem();
+    __syncthreads();  // every wavefront is past its last read of the tiles
+    const uint32_t ost = lds0 + wave * 32 * OROWB;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 val = {dqacc[db][4 * j] * sc, dqacc[db][4 * j + 1] * sc,
                            dqacc[db][4 * j + 2] * sc, dqacc[db][4 * j + 3] * sc};
-        st16f(dq_row + 32 * db + 8 * j + 4 * H, val);
+        const int c = 8 * db + 2 * j + H;
+        *reinterpret_cast<lds_f32x4*>((uintptr_t)(ost + n * OROWB + 16 * (c ^ (n & 7)))) = val;
       }
+    wave_lds_sync();
+    const int rr = lane / CH, cc = lane % CH;
+    const int row0 = q0 + 32 * wave;
+    float* obase = p.dq + ((int64_t)b * Sq + row0) * q_stride + (int64_t)h * D + 4 * cc;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + rr;
+      const f32x4 val =
+          *reinterpret_cast<const lds_f32x4*>((uintptr_t)(ost + r * OROWB + 16 * (cc ^ (r & 7))));
+      if (row0 + r < Sq) st16f_nt(obase + (int64_t)r * q_stride, val);
+    }
   }
 #endif
 }
@@ -634,21 +654,44 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
     if (it < items) step(std::integral_constant<uint32_t, 0>{}, it);
   }
 
-  // dK = scale * dK^T, dV = dV^T: element 4j + i of block db is dcol 32db + 8j + 4H + i
-  if (key < Sk) {
-    float* dk_row = p.dk + ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D;
-    float* dv_row = p.dv + ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D;
+  // dK = scale * dK^T, dV = dV^T: element 4j + i of block jb is dcol
+  // 32 (dh DH + jb) + 8j + 4H + i.  Each wavefront's 32 key rows of its half of d leave
+  // through LDS (dK, then dV, in the Q/dO tile buffers), 16-byte chunks XOR-swizzled by
+  // row, and are stored as whole half rows (128-byte lines) with the non-temporal hint.
+  {
     const float sc = p.scale;
+    constexpr int HD = D / 2, HCH = HD / 4, HROWB = HD * 4, RPI = 64 / HCH;
+    static_assert(8 * 32 * HROWB <= 4 * TILE, "staging fits the tile buffers");
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+    wait_vmem();
+    __syncthreads();  // every wavefront is past its last read of the tiles
+    const uint32_t ost = lds_addr(smem) + wave * 32 * HROWB;
+    const int rr = lane / HCH, cc = lane % HCH;
+    const int krow0 = k0 + 32 * kb;
+    static_for<2>([&](auto KV) {
+      constexpr int kv = decltype(KV)::value;  // 0: dK, 1: dV
 #pragma unroll
-    for (int jb = 0; jb < DH; ++jb)
+      for (int jb = 0; jb < DH; ++jb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = 32 * (dh * DH + jb) + 8 * j + 4 * H;
-        st16f(dk_row + c, f32x4{dkacc[jb][4 * j] * sc, dkacc[jb][4 * j + 1] * sc,
-                                dkacc[jb][4 * j + 2] * sc, dkacc[jb][4 * j + 3] * sc});
-        st16f(dv_row + c, f32x4{dvacc[jb][4 * j], dvacc[jb][4 * j + 1], dvacc[jb][4 * j + 2],
-                                dvacc[jb][4 * j + 3]});
+        for (int j = 0; j < 4; ++j) {
+          const f32x16& a = kv == 0 ? dkacc[jb] : dvacc[jb];
+          const float f = kv == 0 ? sc : 1.f;
+          const f32x4 val = {a[4 * j] * f, a[4 * j + 1] * f, a[4 * j + 2] * f, a[4 * j + 3] * f};
+          const int c = 8 * jb + 2 * j + H;
+          *reinterpret_cast<lds_f32x4*>((uintptr_t)(ost + n * HROWB + 16 * (c ^ (n & 7)))) = val;
+        }
+      wave_lds_sync();
+      float* base = (kv == 0 ? p.dk : p.dv) + ((int64_t)b * Sk + krow0) * kv_stride +
+                    (int64_t)hk * D + dh * HD + 4 * cc;
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = RPI * i + rr;
+        const f32x4 val = *reinterpret_cast<const lds_f32x4*>(
+            (uintptr_t)(ost + r * HROWB + 16 * (cc ^ (r & 7))));
+        if (krow0 + r < Sk) st16f_nt(base + (int64_t)r * kv_stride, val);
       }
+      wave_lds_sync();  // dV's rows overwrite dK's
+    });
   }
 #endif
 }
