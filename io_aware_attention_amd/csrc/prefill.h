@@ -140,9 +140,13 @@ struct PrefillTraits {
   static constexpr int ROWB = D * 2;               // bytes per K/V row in LDS
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int TILE = BN * ROWB;           // bytes per K or V tile
-  static constexpr int kLds = 4 * TILE;            // K and V, double buffered each
+  static constexpr int QTILE = BM * ROWB;          // bytes of the query tile
+  // K and V, double buffered each; the query tile is loaded into V's second buffer and
+  // the QTILE - TILE bytes after it, before that buffer's first V tile
+  static constexpr int kLds = 3 * TILE + QTILE;
   static constexpr int RPB = 256 / ROWB;           // rows per 256-byte bank line
   static constexpr int LOADS = BN * CPR / kThreads;  // 16-byte loads per thread per tile
+  static constexpr int QLOADS = BM * CPR / kThreads;  // the same for the query tile
   // swizzle keys: physical chunk = logical chunk ^ key(row)
   static __device__ __forceinline__ int kkey(int r) { return (r / RPB) % CPR; }
   static __device__ __forceinline__ int vkey(int r) { return 4 * ((r / RPB) % (CPR / 4)); }
@@ -223,18 +227,27 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
     return;
   }
 
-  // ---- Q^T fragments (GEMM0 B operand): Q[qrow][16c + 8H .. +7]
-  u32x4 qf[D / 16];
+  // ---- the query tile, straight into LDS like the K/V tiles below: whole rows per load
+  // instruction (loading the Q^T fragments into registers directly takes 32 rows in
+  // 32-byte pieces per instruction, four times the cache-line requests).  Rows past Sq
+  // read as zeros.  Its loads stay in flight with the first K and V tiles'; each wave
+  // reads its fragments once they have all landed.
+  const uint32_t smem_addr = lds_addr(smem);
+  const uint32_t qlds = smem_addr + 3 * TILE;
+  u32x4 qf[D / 16];  // Q^T fragments (GEMM0 B operand), read from LDS before the first tile
   {
-    const uint16_t* qp = p.q + ((int64_t)q_start + qrow) * q_stride + (int64_t)h * D + 8 * H;
+    const int q_row_bytes = p.Hq * D * 2;
+    const int rows = Sq - q0 < BM ? Sq - q0 : BM;
+    const char* qbase =
+        reinterpret_cast<const char*>(p.q) + (((int64_t)q_start + q0) * p.Hq + h) * D * 2;
+    const i32x4 qd = buffer_desc(qbase, (uint32_t)rows * (uint32_t)q_row_bytes);
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(qlds + 1024 * T::QLOADS * wave);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      if (qrow < Sq) qf[c] = ld16(qp + 16 * c);
-      else qf[c] = u32x4{0u, 0u, 0u, 0u};
+    for (int k = 0; k < T::QLOADS; ++k) {
+      const int slot = 64 * (T::QLOADS * wave + k) + lane;
+      const int r = slot / CPR, ph = slot % CPR;
+      buffer_load_lds16(qd, r * q_row_bytes + 16 * (ph ^ T::kkey(r)), l0 + 1024 * k);
     }
-    // The Q loads stay in flight while the first K and V tiles are issued; the
-    // wait_vmem() before the key loop retires both, visibly to the compiler (whose
-    // tracking would otherwise put a wait inside the loop, behind the K/V prefetch).
   }
 
   // ---- direct HBM -> LDS loads.  Wave w, load k fills the 1 KiB LDS block
@@ -253,7 +266,6 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
   // LDS: K tiles in buffers 0/1, V tiles in buffers 2/3.  Tiles are visited from
   // t = n_max - 1 down; tile t uses parity (n_max - 1 - t) & 1, so that the parity of
   // each step of the twice-unrolled key loop is a compile-time constant.
-  const uint32_t smem_addr = lds_addr(smem);
   auto par = [&](int t) { return (n_max - 1 - t) & 1; };
   auto kbuf = [&](int t) { return smem_addr + par(t) * TILE; };
   auto vbuf = [&](int t) { return smem_addr + (2 + par(t)) * TILE; };
@@ -389,8 +401,18 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
     const int w_last_row = (w_rows_end < Sq ? w_rows_end : Sq) - 1;
     skip_first = n_masked > 0 && t - n_min >= 2 && w_last_row + Sk - Sq < t * BN;
   }
-  wait_vmem();  // Q in registers, this wave's share of the tiles in LDS
+  wait_vmem();  // this wave's share of the query tile and of the first tiles in LDS
   __syncthreads();
+  // ---- Q^T fragments: Q[qrow][16c + 8H .. +7], logical chunk 2c + H of the tile's row
+  // qrow - q0 (bank-conflict free, as the K rows)
+  {
+    const int rq = 32 * wave + n;
+    const uint32_t qa = qlds + rq * ROWB;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qf[c] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+          (uintptr_t)(qa + 16 * ((2 * c + H) ^ T::kkey(rq))));
+  }
   // Scores of two consecutive tiles: in a step of parity P, S[P] holds tile t's and
   // S[P ^ 1] receives tile t-1's; the roles swap every step, so nothing is copied.
   f32x16 S[2][2];
@@ -405,7 +427,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
     if (t >= n_mask_lo || t < n_bot) mask(S[0], t);
     mx = rowmax(S[0]);
   }
-  // Every wave has read K of the first tile before the first step refills its buffer.
+  // Every wave has read K of the first tile and its Q fragments before the first step
+  // refills their buffers (the query tile lies in V's second buffer).
   __syncthreads();
 
   // One step (parity P): softmax + PV of tile t; QK^T, mask and row max of tile t-1
