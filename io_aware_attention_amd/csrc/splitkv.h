@@ -11,12 +11,14 @@
 // states are merged through LDS at the end, exactly like the split combine.
 //
 // Products use v_mfma_f32_16x16x32_bf16:
-//   S^T (16 keys x 16 rows) = K . Q^T   A = K rows straight from global memory
+//   S^T (16 keys x 16 rows) = K . Q^T   A = K rows from LDS
 //   O^T (16 dcols x 16 rows) += V^T . P^T, 32 keys per instruction
 // The key rows of the two 16-key blocks are interleaved so that each lane's
 // eight scores are eight consecutive keys, which makes them the P^T operand
-// as they stand.  V goes through a per-wavefront LDS area row by row, as loaded,
-// and GEMM1's V^T fragments come out of it through transposing reads.
+// as they stand.  K and V are loaded as whole rows (16 lanes per 256-byte row, so
+// every load instruction reads full cache lines) and go through per-wavefront LDS
+// areas row by row, as loaded; GEMM0's K fragments come out with 128-bit reads and
+// GEMM1's V^T fragments with transposing reads.
 //
 // Variants (VAR != 0, cache kernels only; the walk-through's Is_local, Has_alibi,
 // Is_softcap): with diag = i + Sk - Sq for query i, the window keeps keys
@@ -77,6 +79,14 @@ struct SplitTraits {
   // is one per-lane base plus an immediate.
   static constexpr int RS = 2 * D + 32;
   static constexpr int WV = TK * RS;               // V area per wavefront
+  // K rows in a wavefront's LDS area at RSK = the row's bytes + 16.  A GEMM0 fragment
+  // read by 8 consecutive lanes touches rows {0, 1, 2, 3, 8, 9, 10, 11} (+ 4 kb) at one
+  // 16-byte chunk; at a 272-byte stride (d = 128) those land on 8 distinct 16-byte
+  // slots of the 256-byte bank line, and the row writes (8 lanes, 128 contiguous
+  // bytes) are conflict-free as well.
+  static constexpr int RSK = 2 * D + 16;
+  static constexpr int WK = TK * RSK;              // K area per wavefront
+  static constexpr int KB = TK * D / 8 / 64;       // 16-byte K loads per lane per step
   static __device__ __forceinline__ int slot(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
   }
@@ -86,7 +96,8 @@ struct SplitTraits {
   // all start on the same bank.
   static constexpr int CD = D + 4;
   static constexpr int kCombine = kWaves * (2 * BMD + BMD * CD) * 4;
-  static constexpr int kLds = kWaves * WV > kCombine ? kWaves * WV : kCombine;
+  static constexpr int kLds =
+      kWaves * (WV + WK) > kCombine ? kWaves * (WV + WK) : kCombine;
 };
 
 template <int D, bool CACHE, int VAR>
@@ -206,6 +217,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   const uint16_t* kbase = p.k + brow * kv_stride + (int64_t)hk * D;
   const uint16_t* vbase = p.v + brow * kv_stride + (int64_t)hk * D;
   const uint32_t wv = lds_addr(smem) + wave * T::WV;
+  const uint32_t wk = lds_addr(smem) + NW * T::WV + wave * T::WK;
   // V addresses (the layout in SplitTraits).  Writes: row 4 kg + r, 16-byte chunk cg of
   // this lane's loads at vw[bi] + RS r.  Reads: GEMM1's A operand for dcols 16 db ..
   // + 15 is two ds_read_b64_tr_b16.  In each 16-lane group g4, source lane nr addresses
@@ -232,17 +244,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   // Software pipeline: each wavefront's loads of its next 32-key step are in
   // flight while the current step is computed (two register sets, swapped by
   // unrolling the loop twice).
-  // Every key and value is read once.  On a dense cache the loads carry the non-temporal
-  // hint (gqa_decode: 5.59 -> 5.82 TB/s); on a paged cache the same hint cost 13%
-  // (5.32 -> 4.63 TB/s with 256-position blocks in random order), so it is left off there.
-  constexpr int kv_policy = CACHE ? 0 : kLoadStreaming;
+  // Every key and value is read once, so the loads carry the non-temporal hint.  With
+  // whole-row loads it pays on a dense and a paged cache alike (paged_decode 190.8 ->
+  // 172.0 us); while K was read as 64-byte pieces of 16 rows per instruction, the hint
+  // cost the paged cache 13% and was left off there.
+  constexpr int kv_policy = kLoadStreaming;
   // Loads go through buffer descriptors that cover rows j0 .. min(j0 + TK, Sk) - 1
   // of this key/value head, so rows past Sk read as zero without a branch.  A cache
   // step (32 aligned keys) lies inside one block, since blocks hold a multiple of 32
   // positions; V rows before the first key read as zero too (an offset of nrec is out
   // of range), because the product with a zero probability must not meet stale data.
   const int kv_row_bytes = p.Hkv * D * 2;
-  auto load_kv = [&](int j0, u32x4 (&kreg)[2][D / 32], u32x4 (&vreg)[VB][4]) {
+  auto load_kv = [&](int j0, u32x4 (&kreg)[T::KB], u32x4 (&vreg)[VB][4]) {
     const int rows = Sk - j0 < TK ? Sk - j0 : TK;
     const int nrec = rows > 0 ? rows * kv_row_bytes : 0;
     int64_t row0 = j0;
@@ -257,12 +270,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
         (void*)(kbase + row0 * kv_stride), (short)0, nrec, 0x00020000);
     const auto rv = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(vbase + row0 * kv_stride), (short)0, nrec, 0x00020000);
+    // K: load i covers rows (lane + 64 i) / (D / 8), whole rows across lanes; rows
+    // before the left padding are loaded as they are (their scores are masked)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        kreg[kb][c] = __builtin_amdgcn_raw_buffer_load_b128(
-            rk, (krow0 + 4 * kb) * kv_row_bytes + (32 * c + 8 * g4) * 2, 0, kv_policy);
+    for (int i = 0; i < T::KB; ++i) {
+      const int blk = lane + 64 * i;
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rk, (blk / (D / 8)) * kv_row_bytes + 16 * (blk % (D / 8)), 0, kv_policy);
+    }
 #pragma unroll
     for (int bi = 0; bi < VB; ++bi) {
       const int blk = lane + 64 * bi;
@@ -275,14 +290,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
       }
     }
   };
-  auto compute = [&](int j0, const u32x4 (&kreg)[2][D / 32], const u32x4 (&vreg)[VB][4]) {
-    // S^T = K . Q^T for the two 16-key blocks; lane element i is key j0 + 8 g4 + 4 kb + i
+  auto compute = [&](int j0, const u32x4 (&kreg)[T::KB], const u32x4 (&vreg)[VB][4]) {
+    typedef __attribute__((address_space(3))) char lds_char;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    // K and V rows into this wavefront's LDS areas, as loaded
+#pragma unroll
+    for (int i = 0; i < T::KB; ++i) {
+      const int blk = lane + 64 * i;
+      *reinterpret_cast<lds_u32x4*>((lds_char*)(uintptr_t)(
+          wk + (blk / (D / 8)) * T::RSK + 16 * (blk % (D / 8)))) = kreg[i];
+    }
+#pragma unroll
+    for (int bi = 0; bi < VB; ++bi) {
+      lds_char* row0 = (lds_char*)(uintptr_t)(wv + vw[bi]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<lds_u32x4*>(row0 + T::RS * r) = vreg[bi][r];
+    }
+    wave_lds_sync();
+    // S^T = K . Q^T for the two 16-key blocks; lane element i is key j0 + 8 g4 + 4 kb + i.
+    // A operand: K[krow0 + 4 kb][32 c + 8 g4 .. + 7]
     f32x4 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) sc[kb] = mfma16(kreg[kb][c], qf[c], sc[kb]);
+      for (int c = 0; c < D / 32; ++c) {
+        const u32x4 ka = *reinterpret_cast<const lds_u32x4*>((const lds_char*)(uintptr_t)(
+            wk + (krow0 + 4 * kb) * T::RSK + 16 * (4 * c + g4)));
+        sc[kb] = mfma16(ka, qf[c], sc[kb]);
+      }
     }
     if constexpr (LOGIT) {
 #pragma unroll
@@ -333,17 +370,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
     for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
     const u32x4 pf = pack8(sc[0][0], sc[0][1], sc[0][2], sc[0][3], sc[1][0], sc[1][1],
                            sc[1][2], sc[1][3]);
-    // V rows into this wavefront's LDS area, as loaded
-#pragma unroll
-    for (int bi = 0; bi < VB; ++bi) {
-      typedef __attribute__((address_space(3))) char lds_char;
-      lds_char* row0 = (lds_char*)(uintptr_t)(wv + vw[bi]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(row0 + T::RS * r) =
-            vreg[bi][r];
-    }
-    wave_lds_sync();
     // O^T += V^T . P^T; A operand: V^T[16 db + nr][8 g4 .. +7]
     static_for<D / 16>([&](auto DB) {
       constexpr int db = decltype(DB)::value;
@@ -356,7 +382,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
   // The prefetch is unconditional (a conditional one would make the compiler wait
   // for it before the current step): past the split's end it re-reads the current
   // step's rows, which the cache still holds.
-  u32x4 kA[2][D / 32], vA[VB][4], kB[2][D / 32], vB[VB][4];
+  u32x4 kA[T::KB], vA[VB][4], kB[T::KB], vB[VB][4];
   int j0 = j_lo + wave * TK;
   if (j0 < j_hi) {
     load_kv(j0, kA, vA);
