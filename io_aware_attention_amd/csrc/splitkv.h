@@ -79,13 +79,17 @@ struct SplitTraits {
   // is one per-lane base plus an immediate.
   static constexpr int RS = 2 * D + 32;
   static constexpr int WV = TK * RS;               // V area per wavefront
-  // K rows in a wavefront's LDS area at RSK = the row's bytes + 16.  A GEMM0 fragment
-  // read by 8 consecutive lanes touches rows {0, 1, 2, 3, 8, 9, 10, 11} (+ 4 kb) at one
-  // 16-byte chunk; at a 272-byte stride (d = 128) those land on 8 distinct 16-byte
-  // slots of the 256-byte bank line, and the row writes (8 lanes, 128 contiguous
-  // bytes) are conflict-free as well.
-  static constexpr int RSK = 2 * D + 16;
+  // K rows in a wavefront's LDS area, unpadded, the 16-byte chunks of row r XOR-swizzled
+  // by kswz(r).  A 128-bit read serves 16 lanes per cycle, and the 16 lanes of a GEMM0
+  // fragment read touch rows {0..3, 8..11, 16..19, 24..27} (+ 4 kb) at one logical
+  // chunk: the swizzle puts them on 16 distinct 16-byte slots of the 256-byte bank line.
+  // A row write (16 lanes, one row's chunks, d = 128; two rows at d = 64) is a
+  // permutation of whole lines, conflict-free as well.
+  static constexpr int RSK = 2 * D;
   static constexpr int WK = TK * RSK;              // K area per wavefront
+  static __device__ __forceinline__ int kswz(int r) {
+    return D == 128 ? (r + 4 * (r >> 4)) & 15 : ((r >> 1) & 1) | (((r >> 3) & 3) << 1);
+  }
   static constexpr int KB = TK * D / 8 / 64;       // 16-byte K loads per lane per step
   static __device__ __forceinline__ int slot(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -297,8 +301,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
 #pragma unroll
     for (int i = 0; i < T::KB; ++i) {
       const int blk = lane + 64 * i;
+      const int r = blk / (D / 8);
       *reinterpret_cast<lds_u32x4*>((lds_char*)(uintptr_t)(
-          wk + (blk / (D / 8)) * T::RSK + 16 * (blk % (D / 8)))) = kreg[i];
+          wk + r * T::RSK + 16 * ((blk % (D / 8)) ^ T::kswz(r)))) = kreg[i];
     }
 #pragma unroll
     for (int bi = 0; bi < VB; ++bi) {
@@ -316,8 +321,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_splitkv(SplitParams p) {
       sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < D / 32; ++c) {
+        const int r = krow0 + 4 * kb;
         const u32x4 ka = *reinterpret_cast<const lds_u32x4*>((const lds_char*)(uintptr_t)(
-            wk + (krow0 + 4 * kb) * T::RSK + 16 * (4 * c + g4)));
+            wk + r * T::RSK + 16 * ((4 * c + g4) ^ T::kswz(r))));
         sc[kb] = mfma16(ka, qf[c], sc[kb]);
       }
     }
