@@ -421,8 +421,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
   constexpr int DH = D / 64;                    // 32-dcol blocks per half of d
   using T = BwdTraits<D, BQ>;
   // Q tiles 0/1, dO tiles 2/3, P, dS, then L2 and D slots 0/1 (1 KiB each: the 64
-  // values use the first 256 bytes, the rest of the load lands as zeros)
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE + 2 * PBUF + 4 * 1024];
+  // values use the first 256 bytes, the rest of the load lands as zeros), then the
+  // staging area of the block's V rows.  The block's K rows are staged in the P and dS
+  // buffers, which the first tile's phase 1 writes only after a workgroup barrier.
+  constexpr int KV_OFF = 4 * TILE;                        // K rows (in P and dS)
+  constexpr int VV_OFF = 4 * TILE + 2 * PBUF + 4 * 1024;  // V rows
+  static_assert(BK * ROWB <= 2 * PBUF, "K rows fit the P and dS buffers");
+  __shared__ __attribute__((aligned(1024))) char smem[VV_OFF + BK * ROWB];
 
   const int total = p.num_n * p.B * p.Hkv;
   const int idx = xcd_remap(blockIdx.x, total);
@@ -466,18 +471,6 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
   const int64_t kv_stride = (int64_t)p.Hkv * D;
   const int q_row_bytes = p.Hq * D * 2;
 
-  // resident K and V fragments of key block kb (B operands of S = Q K^T, dP = dO V^T)
-  u32x4 kf[D / 16], vf[D / 16];
-  {
-    const int64_t off = ((int64_t)b * Sk + key) * kv_stride + (int64_t)hk * D + 8 * H;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      kf[c] = key < Sk ? ld16(p.k + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-      vf[c] = key < Sk ? ld16(p.v + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  }
-
   f32x16 dkacc[DH], dvacc[DH];
 #pragma unroll
   for (int i = 0; i < DH; ++i) {
@@ -486,6 +479,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
   }
 
   if (items > 0) {
+    u32x4 kf[D / 16], vf[D / 16];  // read from LDS once the block's rows have landed (below)
     int loff[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
@@ -645,7 +639,39 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
       });
     };
 
-    issue(0);
+    // Resident K and V fragments of key block kb (B operands of S = Q K^T, dP = dO V^T).
+    // The block's 128 K and V rows go to LDS as whole rows (four rows of 256 bytes per
+    // load instruction at d = 128, in flight with tile 0's loads; rows past Sk land as
+    // zeros), and each lane reads its fragments from there: loaded straight into the
+    // fragment layout, every instruction read 32-byte pieces of 32 rows.
+    {
+      constexpr int KVL = BK * CPR / NT;  // 16-byte loads per thread per tensor
+      const int kv_row_bytes = (int)kv_stride * 2;
+      int koff[KVL];
+#pragma unroll
+      for (int j = 0; j < KVL; ++j) {
+        const int slot = 64 * (KVL * wave + j) + lane;
+        const int r = slot / CPR, ph = slot % CPR;
+        koff[j] = r * kv_row_bytes + 16 * (ph ^ T::swz(r));
+      }
+      const int64_t boff = (((int64_t)b * Sk + k0) * kv_stride + (int64_t)hk * D) * 2;
+      tile_load<KVL>(reinterpret_cast<const char*>(p.k) + boff, Sk - k0, kv_row_bytes, koff,
+                     smem_addr + KV_OFF, wave);
+      tile_load<KVL>(reinterpret_cast<const char*>(p.v) + boff, Sk - k0, kv_row_bytes, koff,
+                     smem_addr + VV_OFF, wave);
+      issue(0);
+      wait_vmem();
+      __syncthreads();  // every wavefront's rows have landed
+      // row 32 kb + n, logical chunk 2c + H; the first step's barrier orders these reads
+      // before phase 1 rewrites the K rows' area
+      const int kr = 32 * kb + n;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const int a = kr * ROWB + 16 * ((2 * c + H) ^ T::swz(kr));
+        kf[c] = lds_b128(smem_addr + KV_OFF + a);
+        vf[c] = lds_b128(smem_addr + VV_OFF + a);
+      }
+    }
     int it = 0;
     for (; it + 1 < items; it += 2) {
       step(std::integral_constant<uint32_t, 0>{}, it);
