@@ -146,7 +146,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
   constexpr int BM = 128, BN = 64;
   using T = BwdTraits<D, BN>;
   constexpr int ROWB = T::ROWB, CPR = T::CPR, TILE = T::TILE, LOADS = T::LOADS;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K 0/1, V 2/3
+  // K tiles 0/1, V tiles 2/3 (before the first tile: the query tile's dO and Q rows),
+  // then D of the tile's 128 rows
+  constexpr int D_OFF = 4 * TILE;
+  static_assert(BM * ROWB <= 2 * TILE, "dO and Q rows fit two tile buffers each");
+  __shared__ __attribute__((aligned(1024))) char smem[D_OFF + BM * 4];
 
   const int total = p.num_m * p.B * p.Hq;
   const int idx = xcd_remap(blockIdx.x, total);
@@ -207,48 +211,99 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
   const int kv_row_bytes = p.Hkv * D * 2;
   float* dq_row = p.dq + ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D;
 
-  // Resident dO^T fragments [qrow][16c + 8H .. +7], and the row scalars: D = sum_c dO_c
-  // O_c (this lane's half of the columns, then the other half from lane l ^ 32) and
-  // L2 = LSE log2(e) (+inf for a row with no visible key).  They go to the workspace for
-  // the dK/dV kernel, which runs next.  Every row below Sq is written, also in tiles that
-  // see no key, since that kernel multiplies P = 0 by (dP - D).
-  // The Q^T fragments (resident too) are loaded alongside, so that all three tensors'
-  // loads are in flight together.
-  const int64_t off = ((int64_t)b * Sq + qrow) * q_stride + (int64_t)h * D + 8 * H;
-  const bool in = qrow < Sq;
-  u32x4 of[D / 16], qf[D / 16];
-  float L2 = INFINITY, Dr = 0.f;
+  // Resident dO^T and Q^T fragments [qrow][16c + 8H .. +7], and the row scalars
+  // D = sum_c dO_c O_c and L2 = LSE log2(e) (+inf for a row with no visible key).  They go
+  // to the workspace for the dK/dV kernel, which runs next.  Every row below Sq is
+  // written, also in tiles that see no key, since that kernel multiplies P = 0 by
+  // (dP - D).  All loads read whole rows: dO and Q go to LDS (four 256-byte rows per load
+  // instruction at d = 128) and the fragments are read from there; O (fp32, needed for D
+  // only) goes to registers 8 lanes per row, one 128-byte line per row and instruction.
+  // Loaded straight into the fragment layout, each instruction read 32-byte pieces of
+  // 32 rows.  Rows past Sq read as zeros.
+  const uint32_t smem_addr = lds_addr(smem);
+  const int rows_q = Sq - q0 < BM ? Sq - q0 : BM;  // rows of the tile below Sq (>= 1)
+  const int q_row_bytes = p.Hq * D * 2;
+  const int64_t qtile = (((int64_t)b * Sq + q0) * p.Hq + h) * D;  // element offset of row q0
   {
-    f32x4 ov[D / 16][2];
+    constexpr int QL = BM * CPR / T::kThreads;  // 16-byte loads per thread per tensor
+    int qoff[QL];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      of[c] = in ? ld16(p.dout + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-      ov[c][0] = in ? *reinterpret_cast<const f32x4*>(p.o + off + 16 * c) : f32x4{};
-      ov[c][1] = in ? *reinterpret_cast<const f32x4*>(p.o + off + 16 * c + 4) : f32x4{};
+    for (int j = 0; j < QL; ++j) {
+      const int slot = 64 * (QL * wave + j) + lane;
+      const int r = slot / CPR, ph = slot % CPR;
+      qoff[j] = r * q_row_bytes + 16 * (ph ^ T::swz(r));
     }
+    tile_load<QL>(reinterpret_cast<const char*>(p.dout + qtile), rows_q, q_row_bytes, qoff,
+                  smem_addr, wave);
+    tile_load<QL>(reinterpret_cast<const char*>(p.q + qtile), rows_q, q_row_bytes, qoff,
+                  smem_addr + 2 * TILE, wave);
+  }
+  // O: pass ps covers rows 32 ps + tid / 8; load j of a lane holds the row's 16-byte chunk
+  // 8 j + tid % 8 (dcols 4 (8 j + tid % 8) .. + 3)
+  constexpr int OJ = D / 32;  // loads per row and lane
+  f32x4 ov[4][OJ];
+  {
+    const auto od = __builtin_amdgcn_make_buffer_rsrc((void*)(p.o + qtile), (short)0,
+                                                      rows_q * (p.Hq * D * 4), 0x00020000);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      qf[c] = in ? ld16(p.q + off + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-    float part[2] = {0.f, 0.f};
+    for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {  // bf16 pair e: element 2e (low half), 2e + 1 (high)
-        const f32x4& o = ov[c][e >> 1];
-        part[0] += __uint_as_float(of[c][e] << 16) * o[2 * (e & 1)];
-        part[1] += __uint_as_float(of[c][e] & 0xffff0000u) * o[2 * (e & 1) + 1];
+      for (int j = 0; j < OJ; ++j) {
+        const int r = 32 * ps + (tid >> 3), c = 8 * j + (tid & 7);
+        ov[ps][j] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       od, r * (p.Hq * D * 4) + 16 * c, 0, 0));
       }
-    Dr = sum_xor32(part[0] + part[1]);
-    if (qrow < Sq) {
-      const float l = p.lse[((int64_t)b * p.Hq + h) * Sq + qrow];
-      L2 = l == -INFINITY ? INFINITY : l * kLog2e;
-      if (H == 0) {
-        const int64_t r = ((int64_t)b * p.Hq + h) * p.sq_pad + qrow;
-        p.dsum[r] = Dr;
-        p.lse2[r] = L2;
+  }
+  const bool in = qrow < Sq;
+  float L2 = INFINITY;
+  if (in) {
+    const float l = p.lse[((int64_t)b * p.Hq + h) * Sq + qrow];
+    L2 = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+  wait_vmem();
+  __syncthreads();  // every wavefront's dO and Q rows have landed
+  // D of rows 32 ps + tid / 8: this lane's 4 OJ products, then the 8 lanes of the row
+  {
+    float* dsh = reinterpret_cast<float*>(smem + D_OFF);
+#pragma unroll
+    for (int ps = 0; ps < 4; ++ps) {
+      const int r = 32 * ps + (tid >> 3);
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < OJ; ++j) {
+        const int c = 8 * j + (tid & 7);  // dcols 4c .. 4c + 3: bf16 chunk c / 2, half c % 2
+        const u32x2 d2 = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+            (uintptr_t)(smem_addr + r * ROWB + 16 * ((c >> 1) ^ T::swz(r)) + 8 * (c & 1)));
+        const f32x4& o = ov[ps][j];
+        acc += __uint_as_float(d2[0] << 16) * o[0];
+        acc += __uint_as_float(d2[0] & 0xffff0000u) * o[1];
+        acc += __uint_as_float(d2[1] << 16) * o[2];
+        acc += __uint_as_float(d2[1] & 0xffff0000u) * o[3];
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      if ((tid & 7) == 0) {
+        dsh[r] = acc;
+        if (r < rows_q) p.dsum[((int64_t)b * p.Hq + h) * p.sq_pad + q0 + r] = acc;
       }
     }
   }
+  // the fragments: row qrow - q0, logical chunk 2c + H
+  u32x4 of[D / 16], qf[D / 16];
+  {
+    const int rq = 32 * wave + n;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const uint32_t a = smem_addr + rq * ROWB + 16 * ((2 * c + H) ^ T::swz(rq));
+      of[c] = lds_b128(a);
+      qf[c] = lds_b128(a + 2 * TILE);
+    }
+  }
+  __syncthreads();  // D complete; every wavefront is past its reads of the dO and Q rows
+  const float Dr = reinterpret_cast<const float*>(smem + D_OFF)[32 * wave + n];
+  if (in && H == 0) p.lse2[((int64_t)b * p.Hq + h) * p.sq_pad + qrow] = L2;
   if (n_max <= n_min) {  // no visible key for any row of this tile: dQ = 0
     if (qrow < Sq) {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -256,8 +311,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
     }
     return;
   }
-
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of ours in flight in the loop
 
   const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)b * Sk * p.Hkv + hk) * D * 2;
   const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)b * Sk * p.Hkv + hk) * D * 2;
@@ -268,7 +321,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
     const int r = slot / CPR, ph = slot % CPR;
     loff[j] = r * kv_row_bytes + 16 * (ph ^ T::swz(r));
   }
-  const uint32_t smem_addr = lds_addr(smem);
   auto issue = [&](int t) {
     const int rows = Sk - t * BN;
     const int64_t toff = (int64_t)t * BN * kv_row_bytes;
