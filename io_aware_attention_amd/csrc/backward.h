@@ -39,6 +39,7 @@ struct BwdParams {
   int sq_pad;        // Sq rounded up to 64: 256-byte aligned rows for the loads into LDS
   int num_m;         // 128-query tiles per (batch, head)
   int num_n;         // 128-key blocks per (batch, kv head)
+  int u_per;         // (batch, kv head) unit slots per XCD: ceil(B * Hkv / 8)
   float scale;       // softmax scale: enters dQ and dK
   float scale_log2;  // scale * log2(e)
   // Variants (VAR of both kernels): window limits (-1 = none), key j visible to query i
@@ -152,10 +153,20 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
   static_assert(BM * ROWB <= 2 * TILE, "dO and Q rows fit two tile buffers each");
   __shared__ __attribute__((aligned(1024))) char smem[D_OFF + BM * 4];
 
-  const int total = p.num_m * p.B * p.Hq;
+  // Work list, as the forward kernel's: each XCD gets u_per (batch, kv head) unit slots
+  // (XCD x: units x, x + 8, ...; slots past the last unit are idle), and inside an XCD
+  // the order is query tile (heaviest first when causal), then unit, then query head of
+  // the unit, so that every XCD starts its longest tiles first.
+  const int total = 8 * p.u_per * p.G * p.num_m;
   const int idx = xcd_remap(blockIdx.x, total);
-  const int bh = idx / p.num_m, mi = idx - bh * p.num_m;
-  const int b = bh / p.Hq, h = bh % p.Hq, hk = h / p.G;
+  const int grp = p.u_per * p.G * p.num_m;
+  const int sg = idx / grp;
+  const int r0 = idx - sg * grp;
+  const int mi = r0 / (p.u_per * p.G);
+  const int rest = r0 - mi * p.u_per * p.G;
+  const int unit = (rest / p.G) * 8 + sg;
+  if (unit >= p.B * p.Hkv) return;  // an idle unit slot
+  const int b = unit / p.Hkv, hk = unit % p.Hkv, h = hk * p.G + rest % p.G;
   const int mblk = CAUSAL ? p.num_m - 1 - mi : mi;  // heaviest causal tiles first
   const int q0 = mblk * BM;
   const int Sq = p.Sq, Sk = p.Sk;
@@ -481,9 +492,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
   static_assert(BK * ROWB <= 2 * PBUF, "K rows fit the P and dS buffers");
   __shared__ __attribute__((aligned(1024))) char smem[VV_OFF + BK * ROWB];
 
-  const int total = p.num_n * p.B * p.Hkv;
+  // Work list: u_per (batch, kv head) unit slots per XCD as in the dQ kernel, and inside
+  // an XCD the order is key block (ascending: the heaviest first when causal), then unit.
+  const int total = 8 * p.u_per * p.num_n;
   const int idx = xcd_remap(blockIdx.x, total);
-  const int unit = idx / p.num_n, nb = idx - unit * p.num_n;
+  const int grp = p.u_per * p.num_n;
+  const int sg = idx / grp;
+  const int r0 = idx - sg * grp;
+  const int nb = r0 / p.u_per;
+  const int unit = (r0 - nb * p.u_per) * 8 + sg;
+  if (unit >= p.B * p.Hkv) return;  // an idle unit slot
   const int b = unit / p.Hkv, hk = unit % p.Hkv;
   const int k0 = nb * BK;
   const int Sq = p.Sq, Sk = p.Sk;

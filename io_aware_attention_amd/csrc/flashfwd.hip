@@ -289,8 +289,10 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, con
   p.sq_pad = (int)sq_pad;
   p.num_m = (int)cdiv(Sq, 128);
   p.num_n = (int)cdiv(Sk, 128);
-  if ((int64_t)p.num_m * B * Hq >= kMaxElems || (int64_t)p.num_n * B * Hkv >= kMaxElems)
-    return FF_ERR_SHAPE;
+  p.u_per = (int)cdiv((int64_t)B * Hkv, 8);
+  const int64_t n_dq = 8 * (int64_t)p.u_per * p.G * p.num_m;  // unit slots of all 8 XCDs
+  const int64_t n_dkdv = 8 * (int64_t)p.u_per * p.num_n;
+  if (n_dq >= kMaxElems || n_dkdv >= kMaxElems) return FF_ERR_SHAPE;
   p.scale = scale;
   p.scale_log2 = scale * ff::kLog2e;
   p.wl = var.wl;
@@ -298,8 +300,8 @@ int attn_bwd_ex(const void* q, const void* k, const void* v, const float* o, con
   p.alibi = var.alibi;
   p.alibi_bstride = var.alibi_bstride;
   hipStream_t s = (hipStream_t)stream;
-  const dim3 g_dq((unsigned)((int64_t)p.num_m * B * Hq));
-  const dim3 g_dkdv((unsigned)((int64_t)p.num_n * B * Hkv));
+  const dim3 g_dq((unsigned)n_dq);
+  const dim3 g_dkdv((unsigned)n_dkdv);
   if (d == 128) launch_bwd<128>(causal != 0, var.var, g_dq, g_dkdv, s, p);
   else launch_bwd<64>(causal != 0, var.var, g_dq, g_dkdv, s, p);
   return launch_status();
