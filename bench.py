@@ -51,10 +51,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 # The device sources each kernel is compiled from (its template code and the shared
 # building blocks); a change to any of them makes its committed counter summary stale.
 KERNEL_SOURCES = {k: [os.path.join(ROOT, "io_aware_attention_amd", "csrc", f) for f in v]
-                  for k, v in {"attn_fwd_prefill": ("device.h", "tiles.h", "prefill.h"),
+                  for k, v in {"attn_fwd_prefill": ("device.h", "tiles.h", "worklist.h", "prefill.h"),
                                "attn_fwd_splitkv": ("device.h", "splitkv.h"),
-                               "attn_bwd_dkdv": ("device.h", "backward.h"),
-                               "attn_fwd_fp8": ("device.h", "fp8.h")}.items()}
+                               "attn_bwd_dkdv": ("device.h", "worklist.h", "backward.h"),
+                               "attn_fwd_fp8": ("device.h", "worklist.h", "fp8.h")}.items()}
 
 
 def log(*a):

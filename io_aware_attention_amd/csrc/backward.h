@@ -20,6 +20,7 @@
 #pragma once
 #include "device.h"
 #include "prefill.h"
+#include "worklist.h"
 
 namespace ff {
 
@@ -153,20 +154,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq(BwdParams p) {
   static_assert(BM * ROWB <= 2 * TILE, "dO and Q rows fit two tile buffers each");
   __shared__ __attribute__((aligned(1024))) char smem[D_OFF + BM * 4];
 
-  // Work list, as the forward kernel's: each XCD gets u_per (batch, kv head) unit slots
-  // (XCD x: units x, x + 8, ...; slots past the last unit are idle), and inside an XCD
-  // the order is query tile (heaviest first when causal), then unit, then query head of
-  // the unit, so that every XCD starts its longest tiles first.
-  const int total = 8 * p.u_per * p.G * p.num_m;
-  const int idx = xcd_remap(blockIdx.x, total);
-  const int grp = p.u_per * p.G * p.num_m;
-  const int sg = idx / grp;
-  const int r0 = idx - sg * grp;
-  const int mi = r0 / (p.u_per * p.G);
-  const int rest = r0 - mi * p.u_per * p.G;
-  const int unit = (rest / p.G) * 8 + sg;
+  // Work list of worklist.h, as the forward kernel's: rank = query tile (heaviest first
+  // when causal), sub = query head of the unit.
+  const int total = kXcds * p.u_per * p.G * p.num_m;
+  const UnitItem item = unit_item(xcd_remap(blockIdx.x, total), p.u_per, p.num_m, p.G);
+  const int unit = item.unit, mi = item.rank;
   if (unit >= p.B * p.Hkv) return;  // an idle unit slot
-  const int b = unit / p.Hkv, hk = unit % p.Hkv, h = hk * p.G + rest % p.G;
+  const int b = unit / p.Hkv, hk = unit % p.Hkv, h = hk * p.G + item.sub;
   const int mblk = CAUSAL ? p.num_m - 1 - mi : mi;  // heaviest causal tiles first
   const int q0 = mblk * BM;
   const int Sq = p.Sq, Sk = p.Sk;
@@ -492,15 +486,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv(BwdParams p) {
   static_assert(BK * ROWB <= 2 * PBUF, "K rows fit the P and dS buffers");
   __shared__ __attribute__((aligned(1024))) char smem[VV_OFF + BK * ROWB];
 
-  // Work list: u_per (batch, kv head) unit slots per XCD as in the dQ kernel, and inside
-  // an XCD the order is key block (ascending: the heaviest first when causal), then unit.
-  const int total = 8 * p.u_per * p.num_n;
-  const int idx = xcd_remap(blockIdx.x, total);
-  const int grp = p.u_per * p.num_n;
-  const int sg = idx / grp;
-  const int r0 = idx - sg * grp;
-  const int nb = r0 / p.u_per;
-  const int unit = (r0 - nb * p.u_per) * 8 + sg;
+  // Work list of worklist.h: rank = key block (ascending: the heaviest first when
+  // causal), one item per unit and rank.
+  const int total = kXcds * p.u_per * p.num_n;
+  const UnitItem item = unit_item(xcd_remap(blockIdx.x, total), p.u_per, p.num_n, 1);
+  const int unit = item.unit, nb = item.rank;
   if (unit >= p.B * p.Hkv) return;  // an idle unit slot
   const int b = unit / p.Hkv, hk = unit % p.Hkv;
   const int k0 = nb * BK;

@@ -26,6 +26,7 @@
 
 #include "device.h"
 #include "prefill.h"
+#include "worklist.h"
 
 namespace ff {
 
@@ -155,15 +156,9 @@ __global__ __launch_bounds__(256, 3) void attn_fwd_fp8(Fp8Params p) {
 
   // ---- work item, in the order of the bf16 prefill kernel (units round-robin over XCDs,
   // heaviest query tiles first)
-  const int idx = xcd_remap(blockIdx.x, p.total);
-  const int grp = p.u_per * p.G * p.num_m;
-  const int sg = idx / grp;
-  const int r0 = idx - sg * grp;
-  const int mi = r0 / (p.u_per * p.G);
-  const int rest = r0 - mi * p.u_per * p.G;
-  const int unit = (rest / p.G) * 8 + sg;
+  const UnitItem item = unit_item(xcd_remap(blockIdx.x, p.total), p.u_per, p.num_m, p.G);
+  const int unit = item.unit, mi = item.rank, hg = item.sub;
   if (unit >= p.B * p.Hkv) return;
-  const int hg = rest % p.G;
   const int hk = unit % p.Hkv;
   const int b = unit / p.Hkv;
   const int h = hk * p.G + hg;

@@ -43,6 +43,7 @@
 
 #include "device.h"
 #include "tiles.h"
+#include "worklist.h"
 
 namespace ff {
 
@@ -85,35 +86,6 @@ __device__ __forceinline__ void seq_range(const int* cu, int b, int total, int* 
 
 // Exponents stay within 2^kRescaleSlack of the stored reference point.
 constexpr float kRescaleSlack = 8.0f;
-
-// The hardware hands consecutive workgroup ids to the 8 XCDs in turn.  Give
-// each XCD one contiguous run of the work list so the workgroups sharing a
-// key/value head also share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int w, int total) {
-  constexpr int kXcd = 8;
-  const int x = w % kXcd, k = w / kXcd;
-  const int q = total / kXcd, r = total % kXcd;
-  return x * q + (x < r ? x : r) + k;
-}
-
-// Work item of workgroup w.  A grid that is resident all at once gets no second round in
-// which short items could fill in behind long ones, and the dispatcher gives the c-th
-// workgroup of an XCD to CU c mod C, again and again.  With the work list heaviest
-// first, CU 0 would then collect the longest item of every round.  For such grids
-// (snake = C) every other round runs backwards, so a CU's long item of one round is
-// followed by a short one of the next.
-__device__ __forceinline__ int work_index(int w, int total, int snake) {
-  if (!snake) return xcd_remap(w, total);
-  constexpr int kXcd = 8;
-  const int x = w % kXcd, k = w / kXcd;
-  const int q = total / kXcd, r = total % kXcd;
-  const int len = q + (x < r);
-  const int round = k / snake, j = k - round * snake;
-  const int left = len - round * snake;
-  const int m = left < snake ? left : snake;  // items in this round
-  const int kk = (round & 1) ? round * snake + (m - 1 - j) : k;
-  return x * q + (x < r ? x : r) + kk;
-}
 
 template <bool B>
 struct MaskTag {
@@ -166,21 +138,11 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void attn_fwd_prefill(FwdPara
   constexpr int LOADS = T::LOADS;
   __shared__ __attribute__((aligned(1024))) char smem[T::kLds];
 
-  // ---- which (batch, head, query tile) this workgroup owns.  Each XCD gets u_per
-  // (batch, kv head) unit slots: XCD x holds units x, x + 8, x + 16, ... of the
-  // batch-major unit list (slots past the last unit are idle), so that the kv heads of
-  // one sequence spread over the XCDs and sequences of different length load them
-  // evenly.  Inside an XCD the order is query tile (heaviest first when causal), then
-  // unit, then query head of the unit, so each XCD starts its longest tiles first.
-  const int idx = work_index(blockIdx.x, p.total, p.snake);
-  const int grp = p.u_per * p.G * p.num_m;
-  const int sg = idx / grp;
-  const int r0 = idx - sg * grp;
-  const int mi = r0 / (p.u_per * p.G);
-  const int rest = r0 - mi * p.u_per * p.G;
-  const int unit = (rest / p.G) * 8 + sg;
+  // ---- which (batch, head, query tile) this workgroup owns (the work list of
+  // worklist.h: rank = query tile, heaviest first when causal; sub = query head)
+  const UnitItem item = unit_item(work_index(blockIdx.x, p.total, p.snake), p.u_per, p.num_m, p.G);
+  const int unit = item.unit, mi = item.rank, hg = item.sub;
   if (unit >= p.B * p.Hkv) return;
-  const int hg = rest % p.G;
   const int hk = unit % p.Hkv;
   const int b = unit / p.Hkv;
   const int h = hk * p.G + hg;
