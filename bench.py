@@ -54,7 +54,8 @@ KERNEL_SOURCES = {k: [os.path.join(ROOT, "io_aware_attention_amd", "csrc", f) fo
                   for k, v in {"attn_fwd_prefill": ("device.h", "tiles.h", "worklist.h", "prefill.h"),
                                "attn_fwd_splitkv": ("device.h", "splitkv.h"),
                                "attn_bwd_dkdv": ("device.h", "worklist.h", "backward.h"),
-                               "attn_fwd_fp8": ("device.h", "worklist.h", "fp8.h")}.items()}
+                               "attn_fwd_fp8": ("device.h", "worklist.h", "fp8.h"),
+                               "attn_kvcache_append": ("device.h", "append.h")}.items()}
 
 
 def log(*a):
@@ -500,6 +501,49 @@ def cpu_oracle(name, seconds, inputs=None):
             "sample": sample + "; algorithmic flops of their visible keys"}
 
 
+def run_append(torch, ff, steps, warmup):
+    """attn_kvcache_append alone: a 2048-position chunk per sequence appended to the paged
+    cache of the paged_decode shape (B=8, Hkv=8, d=128, 256-position blocks, capacity 32768,
+    blocks in a seeded random order), starting at position 15384 (mid-block).  HBM-bound:
+    the new K and V rows are read once and written once."""
+    B, Hkv, d, page, S_new, cap, start = 8, 8, 128, 256, 2048, 32768, 15384
+    mb = cap // page
+    g = torch.Generator(device="cuda:0").manual_seed(5)
+    kn = torch.randn((B, S_new, Hkv, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    vn = torch.randn((B, S_new, Hkv, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    kc = torch.zeros((B * mb, page, Hkv, d), dtype=torch.bfloat16, device="cuda:0")
+    vc = torch.zeros_like(kc)
+    table = torch.from_numpy(np.random.default_rng(5).permutation(B * mb).astype(np.int32)
+                             .reshape(B, mb)).to("cuda:0")
+    seqlens = torch.full((B,), start, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ff.attn_kvcache_append(kn, vn, kc, vc, seqlens, table, B, S_new, Hkv, d, B * mb, page, mb,
+                               stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    t.start()
+    for _ in range(steps):
+        step()
+    ms = t.stop_ms() / steps
+    torch.cuda.synchronize()
+    # spot check: the first new row of batch 0 landed at its logical position
+    blk, row = divmod(start, page)
+    assert torch.equal(kc[int(table[0, blk])][row], kn[0, 0]), "append check failed"
+    nbytes = 4 * B * S_new * Hkv * d * 2  # read k_new, v_new; write both into the cache
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] attn_kvcache_append: {ms * 1e3:.1f} us per launch, {gbs:.0f} GB/s "
+        f"({100 * gbs / PEAK_HBM_GBS:.1f}% of HBM peak)")
+    return {"kernel": "attn_kvcache_append", "workload": "B=8 Hkv=8 d=128, 2048 new positions "
+            "per sequence into 256-position blocks", "us_per_launch": round(ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": nbytes, "GB/s": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "steps": steps, "warmup": warmup}
+
+
 def cpu_baseline(headline_inputs, seconds):
     """The oracle on every configuration (`seconds` split evenly), the headline's entry
     first-class in the JSON line, the host it ran on described."""
@@ -546,6 +590,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=24.0,
                     help="oracle time budget, split over the configurations")
+    ap.add_argument("--append", action="store_true",
+                    help="time attn_kvcache_append alone (a measurement mode, like --copy-mib)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -568,6 +614,10 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": args.steps}), flush=True)
+        return
+
+    if args.append:
+        print(json.dumps(run_append(torch, ff, args.steps, args.warmup)), flush=True)
         return
 
     names = list(synth.WORKLOADS) + list(BWD_SOURCES) if args.workloads == "all" else \
